@@ -1,0 +1,183 @@
+"""Python face of the C ABI: the same three calls, taking torch tensors.
+
+Each ``ep_*`` function checks dtypes, devices, shapes and contiguity (the C
+side trusts buffer sizes), then passes raw device pointers and the current
+HIP stream to libep.so.  Every step of the computation runs in the
+library's kernels; torch only owns the memory and the stream.
+
+``dispatch`` / ``combine`` mirror the pages' call shape
+``dispatch(x, topk_idx, topk_weights, num_experts)`` returning received rows
+and a handle, and ``combine(...)`` reducing back ([P4] "使用示例 › MoE 训练中
+的应用"; [P5] "典型工作流程").
+"""
+
+from collections import namedtuple
+
+import torch
+
+from ._lib import (EP_MAX_EXPERTS, EP_MAX_TOPK, EP_RECV_BF16, EP_RECV_FP8_E4M3_G128, LIB, check)
+
+Handle = namedtuple("Handle", "tokens_per_expert expert_offset slot src_token num_experts")
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(t, name, dtypes, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def ep_layout_workspace_bytes(num_tokens, top_k, num_experts):
+    return int(LIB.ep_layout_workspace_bytes(int(num_tokens), int(top_k), int(num_experts)))
+
+
+def ep_dispatch_layout(topk_idx, num_experts, tokens_per_expert, expert_offset, slot, src_token,
+                       workspace=None, stream=None):
+    _need(topk_idx, "topk_idx", _I32)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T, K]")
+    T, K = topk_idx.shape
+    E = int(num_experts)
+    _need(tokens_per_expert, "tokens_per_expert", _I32, (E,))
+    _need(expert_offset, "expert_offset", _I32, (E + 1,))
+    _need(slot, "slot", _I32, (T, K))
+    _need(src_token, "src_token", _I32, (T * K,))
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8, torch.int32))
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check("ep_dispatch_layout", LIB.ep_dispatch_layout(
+        topk_idx.data_ptr(), T, K, E, tokens_per_expert.data_ptr(), expert_offset.data_ptr(),
+        slot.data_ptr(), src_token.data_ptr(), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def ep_dispatch(x, slot, topk_weights, format, recv_x, recv_scale=None, recv_weight=None, stream=None):
+    _need(x, "x", _BF16)
+    if x.dim() != 2:
+        raise ValueError("x must be [T, H]")
+    T, H = x.shape
+    _need(slot, "slot", _I32)
+    if slot.dim() != 2 or slot.shape[0] != T:
+        raise ValueError("slot must be [T, K]")
+    K = slot.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", _F32, (T, K))
+    if format == EP_RECV_FP8_E4M3_G128:
+        _need(recv_x, "recv_x", _U8, (T * K, H))
+        if H % 128:
+            raise ValueError("FP8 dispatch needs hidden % 128 == 0")
+        _need(recv_scale, "recv_scale", _F32, (T * K, H // 128))
+    elif format == EP_RECV_BF16:
+        _need(recv_x, "recv_x", _BF16, (T * K, H))
+    else:
+        raise ValueError("unknown receive format %r" % (format,))
+    if recv_weight is not None:
+        _need(recv_weight, "recv_weight", _F32, (T * K,))
+    check("ep_dispatch", LIB.ep_dispatch(
+        x.data_ptr(), T, H, K, slot.data_ptr(),
+        topk_weights.data_ptr() if topk_weights is not None else None, int(format), recv_x.data_ptr(),
+        recv_scale.data_ptr() if recv_scale is not None else None,
+        recv_weight.data_ptr() if recv_weight is not None else None, _stream(stream)))
+
+
+def ep_combine(y, slot, topk_weights, out, stream=None):
+    _need(slot, "slot", _I32)
+    if slot.dim() != 2:
+        raise ValueError("slot must be [T, K]")
+    T, K = slot.shape
+    _need(y, "y", _BF16)
+    if y.dim() != 2 or y.shape[0] < T * K:
+        raise ValueError("y must be [>= T*K, H]")
+    H = y.shape[1]
+    _need(topk_weights, "topk_weights", _F32, (T, K))
+    _need(out, "out", _BF16, (T, H))
+    check("ep_combine", LIB.ep_combine(y.data_ptr(), slot.data_ptr(), topk_weights.data_ptr(), T, H, K,
+                                       out.data_ptr(), _stream(stream)))
+
+
+def ep_cast_fp8_e4m3(inp, out, stream=None):
+    _need(inp, "in", _F32)
+    _need(out, "out", _U8, tuple(inp.shape))
+    check("ep_cast_fp8_e4m3", LIB.ep_cast_fp8_e4m3(inp.data_ptr(), out.data_ptr(), inp.numel(),
+                                                   _stream(stream)))
+
+
+# ---- convenience wrappers that allocate their outputs ----------------------
+
+def layout(topk_idx, num_experts, stream=None):
+    """Routing layout of ``topk_idx`` [T, K] (int32 or int64) -> Handle."""
+    if topk_idx.dtype != torch.int32:
+        topk_idx = topk_idx.to(torch.int32)
+    topk_idx = topk_idx.contiguous()
+    T, K = topk_idx.shape
+    E = int(num_experts)
+    if not 1 <= E <= EP_MAX_EXPERTS or not 1 <= K <= EP_MAX_TOPK:
+        raise ValueError("unsupported num_experts=%d / top_k=%d" % (E, K))
+    dev = topk_idx.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+    src = torch.empty(T * K, dtype=torch.int32, device=dev)
+    nb = ep_layout_workspace_bytes(T, K, E)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    ep_dispatch_layout(topk_idx, E, counts, offsets, slot, src, ws, stream)
+    return Handle(counts, offsets, slot, src, E)
+
+
+def dispatch(x, topk_idx, topk_weights, num_experts, fp8=True, handle=None, stream=None):
+    """Permute tokens into expert-major rows.
+
+    Returns (recv_x, recv_scale, recv_weight, handle): recv_x is uint8 E4M3FN
+    [T*K, H] with recv_scale float32 [T*K, H/128] when ``fp8``, else bfloat16
+    [T*K, H] with recv_scale None; recv_weight float32 [T*K] (None if
+    ``topk_weights`` is None).  Rows expert_offset[e] .. expert_offset[e+1]-1
+    belong to expert e.
+    """
+    if handle is None:
+        handle = layout(topk_idx, num_experts, stream)
+    T, H = x.shape
+    K = handle.slot.shape[1]
+    dev = x.device
+    recv_weight = None
+    if topk_weights is not None:
+        topk_weights = topk_weights.to(torch.float32).contiguous()
+        recv_weight = torch.empty(T * K, dtype=torch.float32, device=dev)
+    if fp8:
+        recv_x = torch.empty((T * K, H), dtype=torch.uint8, device=dev)
+        recv_scale = torch.empty((T * K, H // 128), dtype=torch.float32, device=dev)
+        ep_dispatch(x, handle.slot, topk_weights, EP_RECV_FP8_E4M3_G128, recv_x, recv_scale, recv_weight,
+                    stream)
+    else:
+        recv_x = torch.empty((T * K, H), dtype=torch.bfloat16, device=dev)
+        recv_scale = None
+        ep_dispatch(x, handle.slot, topk_weights, EP_RECV_BF16, recv_x, None, recv_weight, stream)
+    return recv_x, recv_scale, recv_weight, handle
+
+
+def combine(y, handle, topk_weights, stream=None):
+    """Weighted reduction of expert outputs ``y`` [T*K, H] (bf16, receive
+    order) back to token order -> bfloat16 [T, H]."""
+    T, K = handle.slot.shape
+    out = torch.empty((T, y.shape[1]), dtype=torch.bfloat16, device=y.device)
+    ep_combine(y, handle.slot, topk_weights.to(torch.float32).contiguous(), out, stream)
+    return out

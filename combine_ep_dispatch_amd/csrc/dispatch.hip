@@ -1,0 +1,207 @@
+// Dispatch: copy every token into its K expert-major receive rows, either
+// quantised to OCP E4M3FN with one binary32 scale per 128 channels, or as
+// the unchanged BF16 bits.
+//
+// [P1 "DeepEP 的常规内核和低延迟内核"]: tokens are sent to their experts in
+// FP8.  Scale rule (not given by the pages): s = RN32(amax / 448) per
+// 128-channel group (1 for an all-zero group, floored at 2^-126), code =
+// E4M3_RNE(RN32(x / s)).
+//
+// gfx950 design: pure data movement, bound by HBM writes (K copies of every
+// token).  The token is the unit of work, never the expert, so skewed
+// routing cannot unbalance the CUs.  Work item = (token, 16 channels) for FP8
+// (two 16-byte loads, one 16-byte store per copy) or (token, 8 channels) for
+// BF16 (one 16-byte load, K 16-byte stores).  Eight consecutive lanes hold
+// one 128-channel group, so the group max is three DPP steps inside the
+// wavefront; the division is IEEE correctly rounded (no reciprocal
+// shortcut), and the conversion is gfx950's OCP FP8 convert.  No LDS, no
+// MFMA.
+
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Receive rows (and weights) of entries k0 .. k0+KC-1 of one token, loaded
+// together before any store so their latencies overlap.
+template <int KC>
+__device__ __forceinline__ void load_rows(const int32_t* __restrict__ srow, const float* __restrict__ wrow,
+                                          int k0, int K, bool want_w, int32_t (&r)[KC], float (&wk)[KC]) {
+#pragma unroll
+  for (int j = 0; j < KC; ++j) {
+    const bool in = k0 + j < K;
+    r[j] = in ? srow[k0 + j] : -1;
+    wk[j] = (in && want_w) ? wrow[k0 + j] : 0.0f;
+  }
+}
+
+template <int KT>
+__global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
+    const uint16_t* __restrict__ x, uint32_t n_items, uint32_t vpt, int32_t H, int32_t Krt,
+    const int32_t* __restrict__ slot, const float* __restrict__ w, uint8_t* __restrict__ recv,
+    float* __restrict__ recv_scale, float* __restrict__ recv_weight) {
+  constexpr int KC = KT > 0 ? KT : 8;  // receive rows handled per pass
+  const int K = KT > 0 ? KT : Krt;
+  const uint32_t item = blockIdx.x * kThreads + threadIdx.x;
+  const bool active = item < n_items;
+  const uint32_t t = active ? item / vpt : 0;
+  const uint32_t v = item - t * vpt;  // 16-channel vector within the token
+  const int32_t* srow = slot + static_cast<size_t>(t) * K;
+  const float* wrow = w + static_cast<size_t>(t) * K;
+  const bool want_w = recv_weight != nullptr && v == 0;
+
+  // issue the receive-row loads first; they overlap the token load and the
+  // quantisation below
+  int32_t r[KC];
+  float wk[KC];
+  if (active) load_rows<KC>(srow, wrow, 0, K, want_w, r, wk);
+
+  u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+  if (active) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * H) + 2 * v;
+    a = src[0];
+    b = src[1];
+  }
+  float f[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(a[i]);
+    f[2 * i + 1] = bf16_hi(a[i]);
+    f[8 + 2 * i] = bf16_lo(b[i]);
+    f[8 + 2 * i + 1] = bf16_hi(b[i]);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+  m = max8_u32(m);  // all 8 lanes of the group now hold its |max| bits
+
+  float s = __uint_as_float(m) / 448.0f;
+  s = s < 0x1p-126f ? 0x1p-126f : s;
+  s = m == 0 ? 1.0f : s;
+
+  u32x4 q;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    q[j] = f32x4_to_e4m3(f[4 * j] / s, f[4 * j + 1] / s, f[4 * j + 2] / s, f[4 * j + 3] / s);
+
+  if (!active) return;
+  const uint32_t G = static_cast<uint32_t>(H) / kGroup;
+  const bool lead = (v & 7) == 0;  // one lane per group writes the scale
+  for (int k0 = 0;;) {
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      if (r[j] < 0) continue;
+      reinterpret_cast<u32x4*>(recv + static_cast<size_t>(r[j]) * H)[v] = q;
+      if (lead) recv_scale[static_cast<size_t>(r[j]) * G + (v >> 3)] = s;
+      if (want_w) recv_weight[r[j]] = wk[j];
+    }
+    k0 += KC;
+    if (k0 >= K) break;
+    load_rows<KC>(srow, wrow, k0, K, want_w, r, wk);
+  }
+}
+
+template <int KT>
+__global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
+    const uint16_t* __restrict__ x, uint32_t n_items, uint32_t vpt, int32_t H, int32_t Krt,
+    const int32_t* __restrict__ slot, const float* __restrict__ w, uint16_t* __restrict__ recv,
+    float* __restrict__ recv_weight) {
+  constexpr int KC = KT > 0 ? KT : 8;
+  const int K = KT > 0 ? KT : Krt;
+  const uint32_t item = blockIdx.x * kThreads + threadIdx.x;
+  if (item >= n_items) return;
+  const uint32_t t = item / vpt;
+  const uint32_t v = item - t * vpt;  // 8-channel vector within the token
+  const int32_t* srow = slot + static_cast<size_t>(t) * K;
+  const float* wrow = w + static_cast<size_t>(t) * K;
+  const bool want_w = recv_weight != nullptr && v == 0;
+  int32_t r[KC];
+  float wk[KC];
+  load_rows<KC>(srow, wrow, 0, K, want_w, r, wk);
+  const u32x4 d = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * H)[v];
+  for (int k0 = 0;;) {
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      if (r[j] < 0) continue;
+      reinterpret_cast<u32x4*>(recv + static_cast<size_t>(r[j]) * H)[v] = d;
+      if (want_w) recv_weight[r[j]] = wk[j];
+    }
+    k0 += KC;
+    if (k0 >= K) break;
+    load_rows<KC>(srow, wrow, k0, K, want_w, r, wk);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void cast_fp8_kernel(const float* __restrict__ in,
+                                                            uint8_t* __restrict__ out, int64_t n) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    const float4 v = *reinterpret_cast<const float4*>(in + i);
+    *reinterpret_cast<uint32_t*>(out + i) = f32x4_to_e4m3(v.x, v.y, v.z, v.w);
+  } else if (i < n) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; i + j < n; ++j) v[j] = in[i + j];
+    const uint32_t c = f32x4_to_e4m3(v[0], v[1], v[2], v[3]);
+    for (int j = 0; i + j < n; ++j) out[i + j] = static_cast<uint8_t>(c >> (8 * j));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_fp8(const uint16_t* x, int32_t T, int32_t H, int32_t K, const int32_t* slot,
+                               const float* w, uint8_t* recv, float* recv_scale, float* recv_weight,
+                               hipStream_t stream) {
+  const uint32_t vpt = static_cast<uint32_t>(H) / 16;
+  const uint32_t n_items = static_cast<uint32_t>(T) * vpt;
+  if (n_items == 0) return hipSuccess;
+  const dim3 grid((n_items + kThreads - 1) / kThreads), block(kThreads);
+#define EP_DISPATCH_FP8(KV)                                                                        \
+  hipLaunchKernelGGL(dispatch_fp8_kernel<KV>, grid, block, 0, stream, x, n_items, vpt, H, K, slot, w, \
+                     recv, recv_scale, recv_weight)
+  switch (K) {
+    case 1: EP_DISPATCH_FP8(1); break;
+    case 2: EP_DISPATCH_FP8(2); break;
+    case 4: EP_DISPATCH_FP8(4); break;
+    case 6: EP_DISPATCH_FP8(6); break;
+    case 8: EP_DISPATCH_FP8(8); break;
+    default: EP_DISPATCH_FP8(0); break;
+  }
+#undef EP_DISPATCH_FP8
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_bf16(const uint16_t* x, int32_t T, int32_t H, int32_t K, const int32_t* slot,
+                                const float* w, uint16_t* recv, float* recv_weight, hipStream_t stream) {
+  const uint32_t vpt = static_cast<uint32_t>(H) / 8;
+  const uint32_t n_items = static_cast<uint32_t>(T) * vpt;
+  if (n_items == 0) return hipSuccess;
+  const dim3 grid((n_items + kThreads - 1) / kThreads), block(kThreads);
+#define EP_DISPATCH_BF16(KV)                                                                        \
+  hipLaunchKernelGGL(dispatch_bf16_kernel<KV>, grid, block, 0, stream, x, n_items, vpt, H, K, slot, w, \
+                     recv, recv_weight)
+  switch (K) {
+    case 1: EP_DISPATCH_BF16(1); break;
+    case 2: EP_DISPATCH_BF16(2); break;
+    case 4: EP_DISPATCH_BF16(4); break;
+    case 6: EP_DISPATCH_BF16(6); break;
+    case 8: EP_DISPATCH_BF16(8); break;
+    default: EP_DISPATCH_BF16(0); break;
+  }
+#undef EP_DISPATCH_BF16
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_fp8(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t threads = (n + 3) / 4;
+  const dim3 grid(static_cast<uint32_t>((threads + kThreads - 1) / kThreads)), block(kThreads);
+  hipLaunchKernelGGL(cast_fp8_kernel, grid, block, 0, stream, in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace ep

@@ -1,0 +1,119 @@
+// C ABI of the MoE dispatch/combine library: argument checks, then kernel
+// launches on the caller's stream.  See include/ep.h for the contract.
+
+#include "../../include/ep.h"
+
+#include <hip/hip_runtime.h>
+
+#include "ep_internal.h"
+
+#define EP_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Largest T*K handled: bounds the per-key scan over chunks in the layout's
+// second pass (at most 1024 chunks of 4096 entries).
+constexpr int64_t kMaxRows = int64_t(1) << 22;
+
+ep_status from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+ep_status check_common(int64_t T, int32_t K) {
+  if (T < 0 || K < 1) return EP_ERR_INVALID_ARG;
+  if (K > EP_MAX_TOPK) return EP_ERR_UNSUPPORTED;
+  if (T * K >= (int64_t(1) << 31)) return EP_ERR_INVALID_ARG;
+  if (T * K > kMaxRows) return EP_ERR_UNSUPPORTED;
+  return EP_OK;
+}
+
+}  // namespace
+
+EP_API const char* ep_status_string(int status) {
+  switch (status) {
+    case EP_OK: return "EP_OK";
+    case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
+    case EP_ERR_UNSUPPORTED: return "EP_ERR_UNSUPPORTED";
+    case EP_ERR_HIP: return "EP_ERR_HIP";
+    default: return "EP_ERR_UNKNOWN";
+  }
+}
+
+EP_API size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t top_k, int32_t num_experts) {
+  if (num_tokens < 0 || top_k < 1 || num_experts < 1 || num_experts > EP_MAX_EXPERTS) return 0;
+  return ep::layout_workspace_bytes(num_tokens * top_k, num_experts);
+}
+
+EP_API ep_status ep_dispatch_layout(const int32_t* topk_idx, int64_t num_tokens, int32_t top_k,
+                                    int32_t num_experts, int32_t* tokens_per_expert, int32_t* expert_offset,
+                                    int32_t* slot, int32_t* src_token, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  ep_status st = check_common(num_tokens, top_k);
+  if (st != EP_OK) return st;
+  if (num_experts < 1) return EP_ERR_INVALID_ARG;
+  if (num_experts > EP_MAX_EXPERTS) return EP_ERR_UNSUPPORTED;
+  if (!tokens_per_expert || !expert_offset) return EP_ERR_INVALID_ARG;
+  if (!aligned(tokens_per_expert, 4) || !aligned(expert_offset, 4)) return EP_ERR_INVALID_ARG;
+  const int64_t rows = num_tokens * top_k;
+  if (rows > 0) {
+    if (!topk_idx || !slot || !src_token) return EP_ERR_INVALID_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(slot, 4) || !aligned(src_token, 4)) return EP_ERR_INVALID_ARG;
+  }
+  const size_t need = ep::layout_workspace_bytes(rows, num_experts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return EP_ERR_INVALID_ARG;
+  return from_hip(ep::launch_layout(topk_idx, static_cast<int32_t>(rows), top_k, num_experts,
+                                    tokens_per_expert, expert_offset, slot, src_token, workspace,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+EP_API ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                             const int32_t* slot, const float* topk_weights, int32_t format, void* recv_x,
+                             float* recv_scale, float* recv_weight, void* stream) {
+  ep_status st = check_common(num_tokens, top_k);
+  if (st != EP_OK) return st;
+  if (hidden <= 0) return EP_ERR_INVALID_ARG;
+  if (format != EP_RECV_FP8_E4M3_G128 && format != EP_RECV_BF16) return EP_ERR_INVALID_ARG;
+  if (format == EP_RECV_FP8_E4M3_G128 && hidden % 128 != 0) return EP_ERR_INVALID_ARG;
+  if (hidden % 8 != 0) return EP_ERR_INVALID_ARG;
+  if (recv_weight != nullptr && topk_weights == nullptr) return EP_ERR_INVALID_ARG;
+  if (num_tokens * hidden >= (int64_t(1) << 35)) return EP_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return EP_OK;
+  if (!x || !slot || !recv_x) return EP_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(slot, 4)) return EP_ERR_INVALID_ARG;
+  if (topk_weights && !aligned(topk_weights, 4)) return EP_ERR_INVALID_ARG;
+  if (recv_weight && !aligned(recv_weight, 4)) return EP_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t T = static_cast<int32_t>(num_tokens);
+  if (format == EP_RECV_FP8_E4M3_G128) {
+    if (!recv_scale || !aligned(recv_scale, 4)) return EP_ERR_INVALID_ARG;
+    return from_hip(ep::launch_dispatch_fp8(static_cast<const uint16_t*>(x), T, hidden, top_k, slot,
+                                            topk_weights, static_cast<uint8_t*>(recv_x), recv_scale,
+                                            recv_weight, s));
+  }
+  return from_hip(ep::launch_dispatch_bf16(static_cast<const uint16_t*>(x), T, hidden, top_k, slot,
+                                           topk_weights, static_cast<uint16_t*>(recv_x), recv_weight, s));
+}
+
+EP_API ep_status ep_combine(const void* y, const int32_t* slot, const float* topk_weights, int64_t num_tokens,
+                            int32_t hidden, int32_t top_k, void* out, void* stream) {
+  ep_status st = check_common(num_tokens, top_k);
+  if (st != EP_OK) return st;
+  if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARG;
+  if (num_tokens * hidden >= (int64_t(1) << 35)) return EP_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return EP_OK;
+  if (!y || !slot || !topk_weights || !out) return EP_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(slot, 4) || !aligned(topk_weights, 4))
+    return EP_ERR_INVALID_ARG;
+  return from_hip(ep::launch_combine(static_cast<const uint16_t*>(y), slot, topk_weights,
+                                     static_cast<int32_t>(num_tokens), hidden, top_k,
+                                     static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+}
+
+EP_API ep_status ep_cast_fp8_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (n < 0) return EP_ERR_INVALID_ARG;
+  if (n >= (int64_t(1) << 40)) return EP_ERR_UNSUPPORTED;
+  if (n == 0) return EP_OK;
+  if (!in || !out || !aligned(in, 16) || !aligned(out, 16)) return EP_ERR_INVALID_ARG;
+  return from_hip(ep::launch_cast_fp8(in, out, n, static_cast<hipStream_t>(stream)));
+}

@@ -1,0 +1,32 @@
+// Host-side launchers for the kernels (internal; the C ABI in ep_api.hip
+// validates arguments and then calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+// Layout: chooses the single-workgroup path or the two-kernel multi-block
+// path from the shape.
+size_t layout_workspace_bytes(int64_t rows, int32_t num_experts);
+hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, int32_t num_experts,
+                         int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
+                         void* workspace, hipStream_t stream);
+
+hipError_t launch_dispatch_fp8(const uint16_t* x, int32_t num_tokens, int32_t hidden, int32_t top_k,
+                               const int32_t* slot, const float* topk_weights, uint8_t* recv,
+                               float* recv_scale, float* recv_weight, hipStream_t stream);
+
+hipError_t launch_dispatch_bf16(const uint16_t* x, int32_t num_tokens, int32_t hidden, int32_t top_k,
+                                const int32_t* slot, const float* topk_weights, uint16_t* recv,
+                                float* recv_weight, hipStream_t stream);
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* topk_weights,
+                          int32_t num_tokens, int32_t hidden, int32_t top_k, uint16_t* out,
+                          hipStream_t stream);
+
+hipError_t launch_cast_fp8(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+
+}  // namespace ep

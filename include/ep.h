@@ -1,0 +1,169 @@
+/*
+ * ep.h - MoE token dispatch / combine on one MI355X (gfx950): C ABI.
+ *
+ * The pages this library follows describe DeepSeek's DeepEP:
+ *   [P1] "DeepSeek 开源周第二弹：DeepEP —— 首个 MoE 模型训练和推理的 EP 通信库"
+ *        (m.youleyou.com), sections "DeepEP 的核心功能" and
+ *        "DeepEP 的常规内核和低延迟内核";
+ *   [P4] the DeepEP article on deepseek.csdn.net, sections
+ *        "使用示例 › MoE 训练中的应用" and "使用示例 › 推理解码阶段的应用";
+ *   [P5] "deepseek-ai/DeepEP" (agentlenshq.com), section "典型工作流程".
+ * There, dispatch(x, topk_idx, topk_weights, num_experts) sends every token
+ * to the experts it is routed to and returns the received rows plus a
+ * handle; combine uses the handle to reduce the expert outputs back to the
+ * tokens.  On one GPU all experts are resident, so "send" becomes a
+ * permutation into an expert-major receive buffer in the same HBM, and the
+ * handle is the routing layout below.  The pages' single dispatch call is
+ * split into ep_dispatch_layout (routing metadata) and ep_dispatch (the
+ * data movement); ep_combine is the reduction.
+ *
+ * Conventions for every call
+ *   - All array arguments are DEVICE pointers to contiguous row-major
+ *     memory owned by the caller.  The library allocates nothing, keeps no
+ *     state between calls and is safe to call from several host threads.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *     call only enqueues work on it and returns; nothing synchronises with
+ *     the host.  Results are valid once the stream reaches that point.
+ *   - Arguments are checked on the host before anything is launched.  On
+ *     an error the call returns a non-zero ep_status and has enqueued
+ *     nothing.  EP_ERR_HIP means a launch was refused by the runtime.
+ *   - Notation: T tokens, K experts per token (top-k), E experts, H hidden
+ *     channels, R = T*K receive rows, G = H/128 scale groups per row.
+ *   - Expert ids outside [0, E) in topk_idx (for example -1) mark an entry
+ *     as masked: it is not counted, has slot -1, and dispatch and combine
+ *     skip it.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EP_OK = 0,
+  EP_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size */
+  EP_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels handle */
+  EP_ERR_HIP = 3          /* the HIP runtime refused a launch */
+} ep_status;
+
+typedef enum {
+  /* OCP E4M3FN bytes [R, H] plus one binary32 scale per 128 channels
+   * [R, G]; requires H % 128 == 0. */
+  EP_RECV_FP8_E4M3_G128 = 0,
+  /* the token's BF16 bits copied unchanged [R, H]; requires H % 8 == 0. */
+  EP_RECV_BF16 = 1
+} ep_recv_format;
+
+#define EP_MAX_EXPERTS 1024
+#define EP_MAX_TOPK 32
+
+/* Human-readable name of a status code (static storage). */
+const char* ep_status_string(int status);
+
+/* Bytes of device workspace ep_dispatch_layout needs for this shape
+ * (0 when the single-workgroup path handles it).  Pure host function. */
+size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t top_k, int32_t num_experts);
+
+/*
+ * ep_dispatch_layout - routing layout of one dispatch.
+ *
+ * Defines the handle of [P4 "使用示例 › MoE 训练中的应用"] and the
+ * per-expert received count of [P4 "使用示例 › 推理解码阶段的应用"].  The
+ * pages leave the order inside an expert open; here it is ascending token
+ * index (ascending k inside a token), which makes every output
+ * deterministic:
+ *
+ *   tokens_per_expert[e] = #{(t,k) : topk_idx[t,k] == e}
+ *   expert_offset[0] = 0, expert_offset[e+1] = expert_offset[e] + tokens_per_expert[e]
+ *   slot[t,k] = expert_offset[e] + #{(t',k') before (t,k) in (t,k) order with expert e}
+ *               (-1 for a masked entry)
+ *   src_token[slot[t,k]] = t, and src_token[r] = -1 for r >= expert_offset[E]
+ *
+ * topk_idx          int32 [T, K] in
+ * tokens_per_expert int32 [E]    out
+ * expert_offset     int32 [E+1]  out (expert_offset[E] = number of unmasked entries)
+ * slot              int32 [T, K] out (the handle's forward map)
+ * src_token         int32 [T*K]  out (the handle's inverse map)
+ * workspace         device scratch of >= ep_layout_workspace_bytes(T, K, E)
+ *                   bytes, 16-byte aligned (may be NULL when that is 0);
+ *                   its contents are clobbered.
+ * Requirements: T >= 0, 1 <= K <= EP_MAX_TOPK, 1 <= E <= EP_MAX_EXPERTS,
+ * T*K < 2^31, int32 arrays 4-byte aligned.  T == 0 writes zero counts and
+ * offsets.
+ */
+ep_status ep_dispatch_layout(const int32_t* topk_idx, int64_t num_tokens, int32_t top_k,
+                             int32_t num_experts, int32_t* tokens_per_expert,
+                             int32_t* expert_offset, int32_t* slot, int32_t* src_token,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ep_dispatch - copy every token into its K receive rows.
+ *
+ * [P1 "DeepEP 的常规内核和低延迟内核"]: dispatch moves tokens to their
+ * experts in FP8.  The per-128-channel granularity and the scale formula
+ * are not given by the pages; this library uses, per token t and group g
+ * of 128 channels:
+ *   a = max |x[t,c]|,  s = RN32(a / 448)  (s = 1 if a == 0; s = 2^-126 if
+ *   a / 448 would be below 2^-126),
+ *   q[c] = E4M3FN_RNE(RN32(x[t,c] / s))   (one correctly rounded division)
+ * and for each unmasked k with r = slot[t,k]:
+ *   recv_x[r, :] = q,  recv_scale[r, g] = s,  recv_weight[r] = topk_weights[t,k].
+ * With EP_RECV_BF16, recv_x[r, :] = x[t, :] bit for bit and recv_scale is
+ * unused (may be NULL).
+ *
+ * x            bf16 bits [T, H] in, 16-byte aligned
+ * slot         int32 [T, K] from ep_dispatch_layout
+ * topk_weights float32 [T, K] or NULL (then recv_weight must be NULL)
+ * recv_x       [R, H] out: uint8 (FP8) or bf16 bits, 16-byte aligned
+ * recv_scale   float32 [R, G] out (FP8 only), 4-byte aligned
+ * recv_weight  float32 [R] out or NULL
+ * Rows r >= expert_offset[E] (there are none unless entries are masked)
+ * are left untouched.  Requirements: H > 0, H % 128 == 0 for FP8,
+ * H % 8 == 0 for BF16, 1 <= K <= EP_MAX_TOPK, T*K < 2^31,
+ * T*K*H < 2^47 bytes of receive data.
+ */
+ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                      const int32_t* slot, const float* topk_weights, int32_t format,
+                      void* recv_x, float* recv_scale, float* recv_weight, void* stream);
+
+/*
+ * ep_combine - reduce each token's K expert outputs back to the token.
+ *
+ * [P5 "典型工作流程"]: combine reduces the expert outputs back to the
+ * source; [P1 "DeepEP 的常规内核和低延迟内核"]: in BF16.  Arithmetic
+ * (not fixed by the pages): binary32, ascending k, product rounded before
+ * the add (no fused multiply-add), starting from +0.0, result rounded once
+ * to BF16 (round to nearest even):
+ *   acc = +0.0; for k with r = slot[t,k] >= 0:
+ *       acc = RN32(acc + RN32(topk_weights[t,k] * y[r,c]))
+ *   out[t,c] = BF16_RNE(acc)
+ *
+ * y            bf16 bits [>= R, H] in (receive-row order), 16-byte aligned
+ * slot         int32 [T, K] from ep_dispatch_layout
+ * topk_weights float32 [T, K]
+ * out          bf16 bits [T, H] out, 16-byte aligned; must not overlap y
+ * Requirements: H > 0, H % 8 == 0, 1 <= K <= EP_MAX_TOPK, T*K < 2^31.
+ */
+ep_status ep_combine(const void* y, const int32_t* slot, const float* topk_weights,
+                     int64_t num_tokens, int32_t hidden, int32_t top_k, void* out,
+                     void* stream);
+
+/*
+ * ep_cast_fp8_e4m3 - the binary32 -> E4M3FN conversion ep_dispatch uses,
+ * applied elementwise: out[i] = E4M3FN_RNE_satfinite(in[i]).  Magnitudes
+ * beyond 448 saturate to +-448; NaN inputs are outside the contract.
+ * Exposed so the conversion can be checked exhaustively against its
+ * definition (OCP 8-bit floating point specification v1.0).
+ * in float32 [n], out uint8 [n]; n >= 0; both 16-byte aligned.
+ */
+ep_status ep_cast_fp8_e4m3(const float* in, uint8_t* out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

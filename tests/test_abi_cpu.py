@@ -1,0 +1,109 @@
+"""The C-ABI library loads and exports what include/ep.h declares (CPU only).
+
+Only host-side paths run here: argument checks that return before any
+launch, the workspace-size query and the status strings.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import combine_ep_dispatch_amd as ep
+
+    return ep
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for f in ("ep_dispatch_layout", "ep_dispatch", "ep_combine"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert set(declared_functions()) == set(lib._lib.EXPORTS)
+
+
+def test_status_strings(lib):
+    s = lib.LIB.ep_status_string
+    assert s(0) == b"EP_OK" and s(1) == b"EP_ERR_INVALID_ARG"
+    assert s(2) == b"EP_ERR_UNSUPPORTED" and s(3) == b"EP_ERR_HIP" and s(99) == b"EP_ERR_UNKNOWN"
+
+
+def test_workspace_bytes(lib):
+    f = lib.ep_layout_workspace_bytes
+    assert f(64, 2, 16) == 0          # single workgroup
+    assert f(128, 8, 256) == 0
+    assert f(512, 8, 256) == 0        # 4096 entries: still one workgroup
+    assert f(4096, 8, 256) == 32 * 257 * 4  # 32 chunks of 1024 entries
+    assert f(32768, 8, 256) == 64 * 257 * 4  # 64 chunks of 4096 entries
+    assert f(-1, 8, 256) == 0 and f(10, 0, 4) == 0 and f(10, 2, 2000) == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def test_layout_rejects_bad_arguments(lib):
+    L = lib.LIB.ep_dispatch_layout
+    ok = dict(idx=FAKE, T=4, K=2, E=8, c=FAKE, o=FAKE, s=FAKE, r=FAKE, ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L(a["idx"], a["T"], a["K"], a["E"], a["c"], a["o"], a["s"], a["r"], a["ws"], a["wsb"], None)
+
+    assert call(K=0) == lib.EP_ERR_INVALID_ARG
+    assert call(T=-1) == lib.EP_ERR_INVALID_ARG
+    assert call(E=0) == lib.EP_ERR_INVALID_ARG
+    assert call(E=1025) == lib.EP_ERR_UNSUPPORTED
+    assert call(K=33) == lib.EP_ERR_UNSUPPORTED
+    assert call(c=None) == lib.EP_ERR_INVALID_ARG
+    assert call(idx=None) == lib.EP_ERR_INVALID_ARG
+    assert call(s=FAKE + 2) == lib.EP_ERR_INVALID_ARG  # misaligned int32
+    assert call(T=1 << 20, K=8) == lib.EP_ERR_UNSUPPORTED  # beyond 2**22 entries
+    # multi-block shapes need a workspace
+    assert call(T=4096, K=8, E=256) == lib.EP_ERR_INVALID_ARG
+    assert call(T=4096, K=8, E=256, ws=FAKE, wsb=100) == lib.EP_ERR_INVALID_ARG
+
+
+def test_dispatch_and_combine_reject_bad_arguments(lib):
+    D = lib.LIB.ep_dispatch
+    C = lib.LIB.ep_combine
+    fp8, bf16 = lib.EP_RECV_FP8_E4M3_G128, lib.EP_RECV_BF16
+    assert D(FAKE, 4, 200, 2, FAKE, None, fp8, FAKE, FAKE, None, None) == lib.EP_ERR_INVALID_ARG  # H%128
+    assert D(FAKE, 4, 130, 2, FAKE, None, bf16, FAKE, None, None, None) == lib.EP_ERR_INVALID_ARG  # H%8
+    assert D(FAKE, 4, 256, 2, FAKE, None, 7, FAKE, FAKE, None, None) == lib.EP_ERR_INVALID_ARG
+    assert D(FAKE, 4, 256, 2, FAKE, None, fp8, FAKE, None, None, None) == lib.EP_ERR_INVALID_ARG  # no scale
+    assert D(FAKE + 8, 4, 256, 2, FAKE, None, fp8, FAKE, FAKE, None, None) == lib.EP_ERR_INVALID_ARG
+    assert D(FAKE, 4, 256, 2, FAKE, None, fp8, FAKE, FAKE, FAKE, None) == lib.EP_ERR_INVALID_ARG  # w needed
+    assert D(None, 0, 256, 2, None, None, fp8, None, None, None, None) == lib.EP_OK  # T == 0: no-op
+    assert C(FAKE, FAKE, FAKE, 4, 12, 2, FAKE, None) == lib.EP_ERR_INVALID_ARG  # H%8
+    assert C(FAKE, FAKE, None, 4, 16, 2, FAKE, None) == lib.EP_ERR_INVALID_ARG
+    assert C(FAKE, FAKE, FAKE, 4, 16, 0, FAKE, None) == lib.EP_ERR_INVALID_ARG
+    assert C(None, None, None, 0, 16, 2, None, None) == lib.EP_OK
+    assert lib.LIB.ep_cast_fp8_e4m3(FAKE, FAKE + 1, 8, None) == lib.EP_ERR_INVALID_ARG
+    assert lib.LIB.ep_cast_fp8_e4m3(None, None, 0, None) == lib.EP_OK
+
+
+def test_product_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "combine_ep_dispatch_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in re.sub(r"#.*|//.*", "", text), f

@@ -1,0 +1,141 @@
+"""GPU edge cases against the oracle: empty, ragged and degenerate inputs,
+runtime-K paths, layout path boundaries, and special values."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_run import SENT_U8, gpu_combine, gpu_dispatch, gpu_layout, host, to_dev
+from workloads import to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def full_check(ep, idx, E, x_bits, y_bits=None, w=None, fp8=True):
+    T, K = idx.shape
+    print("case T=%d K=%d E=%d H=%d fp8=%s" % (T, K, E, x_bits.shape[1], fp8), flush=True)
+    if w is None:
+        w = np.random.default_rng(T * 31 + K).standard_normal((T, K)).astype(np.float32)
+    counts, offsets, slot, src = gpu_layout(ep, idx, E)
+    oc, oo, os_, osrc = oracle.dispatch_layout(idx, E)
+    assert np.array_equal(host(counts), oc)
+    assert np.array_equal(host(offsets), oo)
+    assert np.array_equal(host(slot), os_)
+    assert np.array_equal(host(src), osrc)
+    nv = int(oo[-1])
+    if T == 0:
+        return
+    recv, scale, rw = gpu_dispatch(ep, x_bits, slot, w, fp8=fp8)
+    if fp8:
+        orecv, oscale, orw = oracle.dispatch_fp8(x_bits, os_, topk_weights=w)
+        hr = host(recv)
+        assert np.array_equal(hr[:nv], orecv[:nv])
+        assert np.all(hr[nv:] == SENT_U8)
+        assert np.array_equal(host(scale)[:nv].view(np.uint32), oscale[:nv].view(np.uint32))
+    else:
+        orecv = oracle.dispatch_bf16(x_bits, os_)
+        orw = oracle.dispatch_fp8(x_bits, os_, topk_weights=w)[2] if x_bits.shape[1] % 128 == 0 else None
+        assert np.array_equal(host(recv)[:nv], orecv[:nv])
+    if orw is not None:
+        assert np.array_equal(host(rw)[:nv], orw[:nv])
+    if y_bits is None:
+        y_bits = to_bf16_bits(np.random.default_rng(K).standard_normal((T * K, x_bits.shape[1]), dtype=np.float32))
+    out = host(gpu_combine(ep, y_bits, slot, w))
+    assert np.array_equal(out, oracle.combine(y_bits, os_, w))
+
+
+def rand_x(T, H, seed=0):
+    return to_bf16_bits(np.random.default_rng(seed).standard_normal((T, H), dtype=np.float32))
+
+
+def test_empty_batch(gpu):
+    idx = np.zeros((0, 8), np.int32)
+    full_check(gpu, idx, 256, np.zeros((0, 7168), np.uint16))
+
+
+@pytest.mark.parametrize("T", [1, 3, 37, 129])
+def test_ragged_small(gpu, T):
+    rng = np.random.default_rng(T)
+    idx = np.argsort(rng.random((T, 256)), axis=1)[:, :8].astype(np.int32)
+    full_check(gpu, idx, 256, rand_x(T, 7168, T))
+
+
+@pytest.mark.parametrize("K", [1, 3, 5, 7, 12, 32])
+def test_runtime_and_odd_topk(gpu, K):
+    T, E = 203, 64
+    rng = np.random.default_rng(K)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    full_check(gpu, idx, E, rand_x(T, 384, K))
+    full_check(gpu, idx, E, rand_x(T, 72, K), fp8=False)
+
+
+def test_duplicates_masks_and_out_of_range(gpu):
+    rng = np.random.default_rng(5)
+    T, K, E = 300, 6, 10
+    idx = rng.integers(-3, E + 3, size=(T, K)).astype(np.int32)  # duplicates, -1..-3, >= E
+    full_check(gpu, idx, E, rand_x(T, 256, 5))
+
+
+def test_all_masked(gpu):
+    idx = np.full((50, 4), -1, np.int32)
+    full_check(gpu, idx, 8, rand_x(50, 128, 1))
+
+
+def test_everything_to_one_expert_and_k_equals_e(gpu):
+    T = 3000
+    idx = np.full((T, 1), 17, np.int32)
+    full_check(gpu, idx, 256, rand_x(T, 128, 2))
+    idx = np.tile(np.arange(8, dtype=np.int32)[::-1], (T, 1))  # K == E, every expert every token
+    full_check(gpu, idx, 8, rand_x(T, 128, 3))
+
+
+@pytest.mark.parametrize("E", [1, 2, 255, 257, 1024])
+def test_expert_counts(gpu, E):
+    rng = np.random.default_rng(E)
+    T, K = 700, min(E, 4)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32) if E > 1 else np.zeros((T, 1), np.int32)
+    full_check(gpu, idx, E, rand_x(T, 256, E))
+
+
+@pytest.mark.parametrize("rows", [4095, 4096, 4097, 8200, 65536, 65537, 131072, 131073, 262144])
+def test_layout_path_boundaries(gpu, rows):
+    """Single-workgroup path up to 4096 entries, then 1024-, 2048- and
+    4096-entry chunks; ragged last chunks."""
+    K = 8 if rows % 8 == 0 else 1
+    T = rows // K
+    rng = np.random.default_rng(rows)
+    idx = rng.integers(0, 256, size=(T, K)).astype(np.int32)
+    print("case layout rows", rows, flush=True)
+    counts, offsets, slot, src = gpu_layout(gpu, idx, 256)
+    oc, oo, os_, osrc = oracle.dispatch_layout(idx, 256)
+    assert np.array_equal(host(counts), oc) and np.array_equal(host(offsets), oo)
+    assert np.array_equal(host(slot), os_) and np.array_equal(host(src), osrc)
+
+
+def test_special_values(gpu):
+    """Zero groups, signed zeros, FP8-subnormal outputs, BF16 subnormal
+    inputs, the 2^-126 scale floor, huge magnitudes, exact ties."""
+    T, H = 16, 512
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[0] = 0.0
+    x[1, :128] = -0.0
+    x[1, 128:256] = 0.0
+    x[1, 200] = -0.0
+    x[2, :128] *= np.float32(1e-3)   # wide dynamic range: many FP8 subnormals
+    x[2, 0] = 300.0
+    x[3, :] *= np.float32(2.0 ** -130)  # BF16 subnormals; s floored at 2^-126
+    x[4, :] = np.float32(3.0e38) * np.sign(x[4, :])
+    x[5, :128] = np.float32(448.0)
+    x[5, 1] = np.float32(1.0625 * 448 / 448)  # E4M3 tie after division by s = 1
+    x[6, :128] = np.float32(2.0 ** -140)
+    x[7, :] = np.float32(1e-30) * x[7, :]
+    xb = to_bf16_bits(x)
+    idx = np.stack([np.arange(T) % 5, (np.arange(T) + 2) % 5], axis=1).astype(np.int32)
+    w = rng.standard_normal((T, 2)).astype(np.float32)
+    w[0] = [-0.0, 0.0]
+    w[4] = [0.5, 0.25]  # keeps the huge row's weighted sum finite
+    y = xb[np.repeat(np.arange(T), 2)]
+    full_check(gpu, idx, 5, xb, y_bits=y, w=w)
+    full_check(gpu, idx, 5, xb, y_bits=y, w=w, fp8=False)
