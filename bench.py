@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE dispatch/combine hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: ep_dispatch_layout ->
+ep_dispatch (FP8 E4M3, one scale per 128 channels) -> ep_combine (BF16),
+on the prefill workload of the pages' normal-kernel setting (4096 tokens,
+hidden 7168, 256 experts in 8 groups, top-4 groups, top-8 experts).  Inputs
+are seeded synthetic tensors already resident in HBM when timing starts.
+
+    python bench.py [--steps K] [--warmup W]        # one JSON line
+    python bench.py --profile-pass                  # short run for rocprofv3
+    python bench.py --summarize-profile DIR NAME    # rocprofv3 csv -> profiles/
+
+The JSON line reports throughput as algorithmic bytes per second (bytes the
+method must move, every one of the K copies counted), the per-kernel
+launch durations measured with HIP events on the launch stream, the
+roofline of the dominant kernel (combine), the decode-size (128 tokens)
+step time, and the oracle's CPU throughput on a bounded sample.
+"""
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine µs and achieved HBM GB/s at 4096x7168 top-8; µs at 128 tok"
+PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E peak
+PROFILES = os.path.join(ROOT, "profiles")
+COMBINE_SOURCES = ["combine_ep_dispatch_amd/csrc/combine.hip", "combine_ep_dispatch_amd/csrc/ep_device.h"]
+TRAFFIC_FILE = os.path.join(PROFILES, "combine_prefill_4096x7168_top8_traffic.txt")
+
+
+def alg_bytes(T, H, E, K, fp8=True):
+    """Bytes each kernel must move (reads + writes), all K copies counted."""
+    layout = 12 * T * K + 8 * E + 4  # idx in; slot, src out; counts, offsets out
+    if fp8:
+        dispatch = 2 * T * H + 4 * T * K + T * K * H + 4 * T * K * (H // 128)
+    else:
+        dispatch = 2 * T * H + 4 * T * K + 2 * T * K * H
+    combine = 2 * T * K * H + 8 * T * K + 2 * T * H
+    return layout, dispatch, combine
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Setup:
+    """Device buffers of one workload plus closures for the three calls."""
+
+    def __init__(self, ep, torch, name, seed=0):
+        from workloads import make_workload
+
+        wl = make_workload(name, seed=seed)
+        self.wl = wl
+        T, H, E, K = wl.T, wl.H, wl.E, wl.K
+        dev = "cuda"
+        self.idx = torch.from_numpy(wl.topk_idx).to(dev)
+        self.w = torch.from_numpy(wl.topk_weights).to(dev)
+        self.x = torch.from_numpy(wl.x_bits.view("int16")).to(dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + seed)
+        # expert outputs for combine: independent N(0,1) rows in BF16
+        if wl.fp8:
+            self.y = torch.randn((T * K, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            self.recv = torch.empty((T * K, H), dtype=torch.uint8, device=dev)
+            self.scale = torch.empty((T * K, H // 128), dtype=torch.float32, device=dev)
+            self.fmt = ep.EP_RECV_FP8_E4M3_G128
+        else:
+            self.recv = torch.empty((T * K, H), dtype=torch.bfloat16, device=dev)
+            self.scale = None
+            self.y = self.recv  # identity expert: combine reads the receive buffer
+            self.fmt = ep.EP_RECV_BF16
+        self.counts = torch.empty(E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+        self.src = torch.empty(T * K, dtype=torch.int32, device=dev)
+        nb = ep.ep_layout_workspace_bytes(T, K, E)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.ep = ep
+        self.bytes = alg_bytes(T, H, E, K, wl.fp8)
+
+    def layout(self):
+        self.ep.ep_dispatch_layout(self.idx, self.wl.E, self.counts, self.offsets, self.slot, self.src, self.ws)
+
+    def dispatch(self):
+        self.ep.ep_dispatch(self.x, self.slot, None, self.fmt, self.recv, self.scale, None)
+
+    def combine(self):
+        self.ep.ep_combine(self.y, self.slot, self.w, self.out)
+
+    def step(self):
+        self.layout()
+        self.dispatch()
+        self.combine()
+
+
+def time_steps(torch, s, steps, warmup):
+    """K steps bracketed by synchronisation, timed with HIP events on the
+    stream the kernels are launched on; then the same K steps again with an
+    event between consecutive calls for the per-kernel durations."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        s.step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(steps):
+        s.step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us_step = a.elapsed_time(b) * 1e3 / steps
+
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for m in marks:
+        m[0].record(stream)
+        s.layout()
+        m[1].record(stream)
+        s.dispatch()
+        m[2].record(stream)
+        s.combine()
+        m[3].record(stream)
+    torch.cuda.synchronize()
+    per = {"layout": [], "dispatch": [], "combine": []}
+    for m in marks:
+        per["layout"].append(m[0].elapsed_time(m[1]) * 1e3)
+        per["dispatch"].append(m[1].elapsed_time(m[2]) * 1e3)
+        per["combine"].append(m[2].elapsed_time(m[3]) * 1e3)
+    return us_step, {k: sum(v) / len(v) for k, v in per.items()}, wall
+
+
+def time_graph(torch, s, replays):
+    """Step captured once in a HIP graph and replayed; returns µs per step."""
+    s.step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s.step()
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / replays
+
+
+def read_traffic():
+    """HBM bytes per combine launch from the committed rocprofv3 counter
+    summary, or None when the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != source_hash(COMBINE_SOURCES):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle, untuned, on the same workload: whole passes (layout of all
+    T*K entries, then dispatch + combine of every token in 512-token chunks)
+    repeated until the time budget is spent.  numpy runs these ops on one
+    thread."""
+    import numpy as np
+
+    import oracle
+    from workloads import to_bf16_bits
+
+    T, H, E, K = wl.T, wl.H, wl.E, wl.K
+    step_b = sum(alg_bytes(T, H, E, K, True))
+    chunk = 512
+    y_chunk = to_bf16_bits(np.random.default_rng(7).standard_normal((chunk * K, H), dtype=np.float32))
+    sub_slot = np.arange(chunk * K, dtype=np.int32).reshape(chunk, K)
+    x = wl.x_bits
+    passes = 0
+    t0 = time.perf_counter()
+    while passes == 0 or time.perf_counter() - t0 < budget_s:
+        oracle.dispatch_layout(wl.topk_idx, E)
+        for t in range(0, T, chunk):
+            n = min(chunk, T - t)
+            oracle.dispatch_fp8(x[t:t + n], sub_slot[:n])
+            oracle.combine(y_chunk, sub_slot[:n], wl.topk_weights[t:t + n])
+        passes += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(passes * step_b / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full pass(es) of the same 4096-token workload (layout, FP8 dispatch and combine of "
+                      "every token in 512-token chunks), %.1f s, numpy single-threaded; %d host CPUs visible"
+                      % (passes, dt, os.cpu_count())}
+
+
+def profile_pass(ep, torch):
+    """Short run for rocprofv3: a plain 1 GiB device copy (counter
+    calibration: known bytes read and written), then prefill steps."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    s = Setup(ep, torch, "prefill", 0)
+    for _ in range(5):
+        s.step()
+    torch.cuda.synchronize()
+    print("profile pass done", flush=True)
+
+
+def summarize_profile(dirname, name):
+    """Turn rocprofv3 csv output into short text summaries under profiles/."""
+    import csv
+
+    def rows(pattern):
+        out = []
+        for f in sorted(glob.glob(os.path.join(dirname, "**", pattern), recursive=True)):
+            with open(f) as fh:
+                out += list(csv.DictReader(fh))
+        return out
+
+    stats = rows("*kernel_stats.csv")
+    counters = rows("*counter_collection.csv")
+    lines = []
+    if stats:
+        lines.append("kernel stats (rocprofv3 --kernel-trace --stats):")
+        for r in stats:
+            lines.append("  %-60s calls=%s avg_ns=%s total_ns=%s" % (
+                r.get("Name", "?")[:60], r.get("Calls"), r.get("AverageNs"), r.get("TotalDurationNs")))
+    if counters:
+        agg = {}
+        for r in counters:
+            key = (r.get("Kernel_Name", "?"), r.get("Counter_Name", "?"))
+            agg.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+        lines.append("counters (per dispatch average):")
+        for (k, c), v in sorted(agg.items()):
+            lines.append("  %-60s %-12s n=%d avg=%.1f" % (k[:60], c, len(v), sum(v) / len(v)))
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, name)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(path).read())
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-replays", type=int, default=500)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--summarize-profile", nargs=2, metavar=("DIR", "NAME"))
+    args = ap.parse_args()
+
+    if args.summarize_profile:
+        summarize_profile(*args.summarize_profile)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the path is one GPU's share with every expert resident in its "
+              "HBM, and this build has no multi-GPU transport (requested --gpus %d, WORLD_SIZE %d)"
+              % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import torch
+
+    import combine_ep_dispatch_amd as ep
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    if args.profile_pass:
+        profile_pass(ep, torch)
+        return 0
+
+    s = Setup(ep, torch, "prefill", 0)
+    lay_b, dis_b, com_b = s.bytes
+    us_step, per_kernel, wall = time_steps(torch, s, args.steps, args.warmup)
+    total_b = lay_b + dis_b + com_b
+    gbs = total_b / (us_step * 1e-6) / 1e9
+    graph_us = time_graph(torch, s, 50)
+
+    d = Setup(ep, torch, "decode", 0)
+    d_us, d_per, _ = time_steps(torch, d, 200, 10)
+    d_graph = time_graph(torch, d, args.decode_replays)
+    del d
+
+    comb_us = per_kernel["combine"]
+    achieved = com_b / (comb_us * 1e-6) / 1e9
+    traffic = read_traffic()
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "prefill: 4096 tokens x hidden 7168, 256 experts (8 groups, top-4 groups), "
+                               "top-8, FP8 E4M3 dispatch (1 scale / 128 ch) + BF16 combine, seed 0",
+                   "tokens": s.wl.T, "hidden": s.wl.H, "experts": s.wl.E, "top_k": s.wl.K},
+        "us_per_step": round(us_step, 2),
+        "us_per_step_graph": round(graph_us, 2),
+        "kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
+        "kernel_alg_bytes": {"layout": lay_b, "dispatch": dis_b, "combine": com_b},
+        "decode_128tok_us": {"stream": round(d_us, 2), "graph": round(d_graph, 2),
+                             "kernel_us": {k: round(v, 2) for k, v in d_per.items()}},
+        "roofline": {"bound": "hbm", "kernel": "combine", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(s.wl, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

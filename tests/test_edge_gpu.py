@@ -98,17 +98,20 @@ def test_expert_counts(gpu, E):
     full_check(gpu, idx, E, rand_x(T, 256, E))
 
 
-@pytest.mark.parametrize("rows", [4095, 4096, 4097, 8200, 65536, 65537, 131072, 131073, 262144])
-def test_layout_path_boundaries(gpu, rows):
-    """Single-workgroup path up to 4096 entries, then 1024-, 2048- and
-    4096-entry chunks; ragged last chunks."""
+@pytest.mark.parametrize("rows,E", [(1024, 256), (1025, 256), (4095, 256), (32767, 256), (32768, 256),
+                                    (65536, 256), (65537, 256), (131073, 256), (262144, 256),
+                                    (1024, 1024), (1025, 1024), (65536, 1024), (65537, 1024), (700, 1),
+                                    (5000, 1)])
+def test_layout_path_boundaries(gpu, rows, E):
+    """One workgroup up to 1024 entries, one fused launch up to 65536, then
+    two launches over 4096-entry chunks; ragged last steps and chunks."""
     K = 8 if rows % 8 == 0 else 1
     T = rows // K
     rng = np.random.default_rng(rows)
-    idx = rng.integers(0, 256, size=(T, K)).astype(np.int32)
-    print("case layout rows", rows, flush=True)
-    counts, offsets, slot, src = gpu_layout(gpu, idx, 256)
-    oc, oo, os_, osrc = oracle.dispatch_layout(idx, 256)
+    idx = rng.integers(-1, E, size=(T, K)).astype(np.int32)
+    print("case layout rows", rows, E, flush=True)
+    counts, offsets, slot, src = gpu_layout(gpu, idx, E)
+    oc, oo, os_, osrc = oracle.dispatch_layout(idx, E)
     assert np.array_equal(host(counts), oc) and np.array_equal(host(offsets), oo)
     assert np.array_equal(host(slot), os_) and np.array_equal(host(src), osrc)
 
