@@ -9,7 +9,7 @@ are seeded synthetic tensors already resident in HBM when timing starts.
 
     python bench.py [--steps K] [--warmup W]        # one JSON line
     python bench.py --profile-pass                  # short run for rocprofv3
-    python bench.py --summarize-profile DIR NAME    # rocprofv3 csv -> profiles/
+    python bench.py --summarize-profile DIR         # rocprofv3 csv -> profiles/
 
 The JSON line reports throughput as algorithmic bytes per second (bytes the
 method must move, every one of the K copies counted), the per-kernel
@@ -228,38 +228,82 @@ def profile_pass(ep, torch):
     print("profile pass done", flush=True)
 
 
-def summarize_profile(dirname, name):
-    """Turn rocprofv3 csv output into short text summaries under profiles/."""
+PROFILE_COMMANDS = """\
+cd /tmp && export TMPDIR=/tmp   # then, from the repository root R:
+rocprofv3 --kernel-trace --stats -d R/gpurun_out/prof_trace -o trace --output-format csv -- python3 R/bench.py --profile-pass
+rocprofv3 --pmc FETCH_SIZE -d R/gpurun_out/prof_fetch -o fetch --output-format csv -- python3 R/bench.py --profile-pass
+rocprofv3 --pmc WRITE_SIZE -d R/gpurun_out/prof_write -o write --output-format csv -- python3 R/bench.py --profile-pass
+python3 R/bench.py --summarize-profile R/gpurun_out
+"""
+
+COPY_BYTES = 1 << 30  # the profile pass's plain device copy
+
+
+def summarize_profile(dirname):
+    """rocprofv3 csv output (three runs, see PROFILE_COMMANDS) -> short text
+    summaries under profiles/.  Counters are KiB per dispatch; each is scaled
+    by what it reads for the plain 1 GiB copy (bytes known exactly)."""
     import csv
 
-    def rows(pattern):
+    def rows(sub, pattern):
         out = []
-        for f in sorted(glob.glob(os.path.join(dirname, "**", pattern), recursive=True)):
+        for f in sorted(glob.glob(os.path.join(dirname, sub, "**", pattern), recursive=True)):
             with open(f) as fh:
                 out += list(csv.DictReader(fh))
         return out
 
-    stats = rows("*kernel_stats.csv")
-    counters = rows("*counter_collection.csv")
-    lines = []
-    if stats:
-        lines.append("kernel stats (rocprofv3 --kernel-trace --stats):")
-        for r in stats:
-            lines.append("  %-60s calls=%s avg_ns=%s total_ns=%s" % (
-                r.get("Name", "?")[:60], r.get("Calls"), r.get("AverageNs"), r.get("TotalDurationNs")))
-    if counters:
-        agg = {}
-        for r in counters:
-            key = (r.get("Kernel_Name", "?"), r.get("Counter_Name", "?"))
-            agg.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
-        lines.append("counters (per dispatch average):")
-        for (k, c), v in sorted(agg.items()):
-            lines.append("  %-60s %-12s n=%d avg=%.1f" % (k[:60], c, len(v), sum(v) / len(v)))
+    def short(name):
+        name = name.replace("(anonymous namespace)::", "").replace("void ", "").replace("ep::", "")
+        return name.split("(")[0]
+
+    stats = rows("prof_trace", "*kernel_stats.csv")
+    lines = ["rocprofv3 kernel trace: prefill workload (4096 tokens, hidden 7168, 256 experts, top-8,",
+             "FP8 dispatch, BF16 combine), 5 steps after a 1 GiB device copy", "", "commands:", PROFILE_COMMANDS,
+             "%-40s %6s %12s %12s %12s" % ("kernel", "calls", "avg_ns", "min_ns", "max_ns")]
+    for r in stats:
+        lines.append("%-40s %6s %12.0f %12.0f %12.0f" % (short(r["Name"])[:40], r["Calls"], float(r["AverageNs"]),
+                                                         float(r["MinNs"]), float(r["MaxNs"])))
     os.makedirs(PROFILES, exist_ok=True)
-    path = os.path.join(PROFILES, name)
-    with open(path, "w") as f:
+    with open(os.path.join(PROFILES, "prefill_4096x7168_top8_kernel_trace.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(open(path).read())
+
+    agg = {}
+    for sub, pat in (("prof_fetch", "*counter_collection.csv"), ("prof_write", "*counter_collection.csv")):
+        for r in rows(sub, pat):
+            agg.setdefault((short(r["Kernel_Name"]), r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    avg = {k: sum(v) / len(v) for k, v in agg.items()}
+    copy_kib = COPY_BYTES / 1024.0
+    f_fetch = copy_kib / avg[("__amd_rocclr_copyBuffer", "FETCH_SIZE")]
+    f_write = copy_kib / avg[("__amd_rocclr_copyBuffer", "WRITE_SIZE")]
+    T, H, E, K = 4096, 7168, 256, 8
+    alg = dict(zip(("layout", "dispatch_fp8_kernel", "combine_kernel"), alg_bytes(T, H, E, K, True)))
+    lines = ["HBM traffic per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (two separate --pmc runs),",
+             "prefill workload (4096 x 7168, 256 experts, top-8, FP8 dispatch, BF16 combine).", "",
+             "commands:", PROFILE_COMMANDS,
+             "calibration: plain 1 GiB device copy (__amd_rocclr_copyBuffer) reads FETCH_SIZE %.1f KiB and "
+             "WRITE_SIZE %.1f KiB" % (avg[("__amd_rocclr_copyBuffer", "FETCH_SIZE")],
+                                      avg[("__amd_rocclr_copyBuffer", "WRITE_SIZE")]),
+             "fetch_scale: %.4f" % f_fetch, "write_scale: %.4f" % f_write, ""]
+    comb_total = None
+    for kern in ("layout_fused<16>", "dispatch_fp8_kernel<8>", "combine_kernel<8>"):
+        fk, wk = avg.get((kern, "FETCH_SIZE")), avg.get((kern, "WRITE_SIZE"))
+        if fk is None or wk is None:
+            continue
+        fb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
+        base = kern.split("<")[0]
+        a = alg.get(base) if base != "layout_fused" else alg_bytes(T, H, E, K, True)[0]
+        lines.append("%-24s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
+                     % (kern, fb, wb, fb + wb, a, (fb + wb) / a))
+        if base == "combine_kernel":
+            comb_total = fb + wb
+    lines += ["", "combine kernel (the roofline's dominant kernel):",
+              "hbm_bytes_per_launch: %.0f" % comb_total,
+              "source_sha256: %s" % source_hash(COMBINE_SOURCES),
+              "(sha256 prefix of %s; bench.py reports traffic only while it matches)" % ", ".join(COMBINE_SOURCES)]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    for p in ("prefill_4096x7168_top8_kernel_trace.txt", os.path.basename(TRAFFIC_FILE)):
+        print(open(os.path.join(PROFILES, p)).read())
 
 
 def main():
@@ -271,11 +315,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
-    ap.add_argument("--summarize-profile", nargs=2, metavar=("DIR", "NAME"))
+    ap.add_argument("--summarize-profile", metavar="DIR")
     args = ap.parse_args()
 
     if args.summarize_profile:
-        summarize_profile(*args.summarize_profile)
+        summarize_profile(args.summarize_profile)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -317,12 +317,12 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int p = q0 + u * kThreads + tid;
-      e[u] = (p < R && (p < c0 || p >= c1)) ? idx[p] : -2;
+      e[u] = (p < R && (p < c0 || p >= c1)) ? idx[p] : 0;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (e[u] == -2) continue;
       const int p = q0 + u * kThreads + tid;
+      if (p >= R || (p >= c0 && p < c1)) continue;  // past the end, or this block's own chunk
       const int k = (e[u] >= 0 && e[u] < E) ? e[u] : E;
       atomicAdd(p < c0 ? &before[k] : &after[k], 1);
     }

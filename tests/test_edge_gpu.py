@@ -142,3 +142,22 @@ def test_special_values(gpu):
     y = xb[np.repeat(np.arange(T), 2)]
     full_check(gpu, idx, 5, xb, y_bits=y, w=w)
     full_check(gpu, idx, 5, xb, y_bits=y, w=w, fp8=False)
+
+
+@pytest.mark.parametrize("rows", [900, 1800, 70000])
+def test_masked_ids_of_every_value(gpu, rows):
+    """Masked ids take many values (-1, -2, INT_MIN, E, INT_MAX): each must
+    land in the masked bucket on every layout path (regression: a skip
+    sentinel equal to a legal masked id once dropped entries from the count
+    of masked rows)."""
+    E = 16
+    rng = np.random.default_rng(rows)
+    idx = rng.integers(0, E, size=rows).astype(np.int64)
+    bad = rng.random(rows) < 0.3
+    idx[bad] = rng.choice([-1, -2, -3, E, E + 5, -(2 ** 31), 2 ** 31 - 1], size=int(bad.sum()))
+    idx = idx.astype(np.int32).reshape(-1, 1)
+    print("case masked ids rows", rows, flush=True)
+    counts, offsets, slot, src = gpu_layout(gpu, idx, E)
+    oc, oo, os_, osrc = oracle.dispatch_layout(idx, E)
+    assert np.array_equal(host(counts), oc) and np.array_equal(host(offsets), oo)
+    assert np.array_equal(host(slot), os_) and np.array_equal(host(src), osrc)
