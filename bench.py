@@ -211,9 +211,10 @@ def cpu_baseline(wl, budget_s):
                       % (passes, dt, os.cpu_count())}
 
 
-def profile_pass(ep, torch):
+def profile_pass(ep, torch, workload="prefill"):
     """Short run for rocprofv3: a plain 1 GiB device copy (counter
-    calibration: known bytes read and written), then prefill steps."""
+    calibration: known bytes read and written), then 5 steps of the
+    workload (prefill by default)."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     b = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -221,7 +222,7 @@ def profile_pass(ep, torch):
         b.copy_(a)
     torch.cuda.synchronize()
     del a, b
-    s = Setup(ep, torch, "prefill", 0)
+    s = Setup(ep, torch, workload, 0)
     for _ in range(5):
         s.step()
     torch.cuda.synchronize()
@@ -285,17 +286,17 @@ def summarize_profile(dirname):
                                       avg[("__amd_rocclr_copyBuffer", "WRITE_SIZE")]),
              "fetch_scale: %.4f" % f_fetch, "write_scale: %.4f" % f_write, ""]
     comb_total = None
-    for kern in ("layout_fused<16>", "dispatch_fp8_kernel<8>", "combine_kernel<8>"):
-        fk, wk = avg.get((kern, "FETCH_SIZE")), avg.get((kern, "WRITE_SIZE"))
-        if fk is None or wk is None:
-            continue
-        fb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
-        base = kern.split("<")[0]
-        a = alg.get(base) if base != "layout_fused" else alg_bytes(T, H, E, K, True)[0]
-        lines.append("%-24s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
-                     % (kern, fb, wb, fb + wb, a, (fb + wb) / a))
-        if base == "combine_kernel":
-            comb_total = fb + wb
+    for prefix, a in (("layout", alg_bytes(T, H, E, K, True)[0]), ("dispatch_fp8_kernel", alg["dispatch_fp8_kernel"]),
+                      ("combine_kernel", alg["combine_kernel"])):
+        for kern in sorted({k for (k, c) in avg if k.startswith(prefix)}):
+            fk, wk = avg.get((kern, "FETCH_SIZE")), avg.get((kern, "WRITE_SIZE"))
+            if fk is None or wk is None:
+                continue
+            fb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
+            lines.append("%-24s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
+                         % (kern, fb, wb, fb + wb, a, (fb + wb) / a))
+            if prefix == "combine_kernel":
+                comb_total = fb + wb
     lines += ["", "combine kernel (the roofline's dominant kernel):",
               "hbm_bytes_per_launch: %.0f" % comb_total,
               "source_sha256: %s" % source_hash(COMBINE_SOURCES),
@@ -314,7 +315,8 @@ def main():
     ap.add_argument("--decode-replays", type=int, default=500)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--profile-pass", nargs="?", const="prefill", default=None,
+                    choices=["tiny", "decode", "prefill", "skew", "hbm"])
     ap.add_argument("--summarize-profile", metavar="DIR")
     args = ap.parse_args()
 
@@ -336,7 +338,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         return 1
     if args.profile_pass:
-        profile_pass(ep, torch)
+        profile_pass(ep, torch, args.profile_pass)
         return 0
 
     s = Setup(ep, torch, "prefill", 0)

@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
 // scan of the totals, and an entry's row is offset + before + (own-chunk
 // rank).  Every block reads all T*K ids (from L2 after the first), which
 // trades redundant on-chip work for the second launch and the workspace.
-template <int NW>
+template <int NW, bool V4>
 __global__ __launch_bounds__(NW * kWave) void layout_fused(
     const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src) {
@@ -311,20 +311,50 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
 
   const int c0 = blockIdx.x * kThreads;
   const int c1 = min(R, c0 + kThreads);
-  constexpr int kUnroll = 16;
-  for (int q0 = 0; q0 < R; q0 += kThreads * kUnroll) {
-    int e[kUnroll];
+  // count entry p (outside this block's chunk) into the before/after histogram
+  auto count_one = [&](int p, int e) {
+    if (p >= c0 && p < c1) return;
+    const int k = (e >= 0 && e < E) ? e : E;
+    atomicAdd(p < c0 ? &before[k] : &after[k], 1);
+  };
+  if (V4) {
+    // 16-byte loads: 4 ids each, 8 loads in flight per thread
+    const int4* idx4 = reinterpret_cast<const int4*>(idx);
+    const int n4 = R / 4;
+    constexpr int kUnroll = 8;
+    for (int q0 = 0; q0 < n4; q0 += kThreads * kUnroll) {
+      int4 e[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = q0 + u * kThreads + tid;
-      e[u] = (p < R && (p < c0 || p >= c1)) ? idx[p] : 0;
+      for (int u = 0; u < kUnroll; ++u) {
+        const int q = q0 + u * kThreads + tid;
+        e[u] = q < n4 ? idx4[q] : make_int4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int q = q0 + u * kThreads + tid;
+        if (q >= n4) continue;
+        count_one(4 * q, e[u].x);
+        count_one(4 * q + 1, e[u].y);
+        count_one(4 * q + 2, e[u].z);
+        count_one(4 * q + 3, e[u].w);
+      }
     }
+    const int p = 4 * n4 + tid;  // the last R % 4 ids
+    if (p < R) count_one(p, idx[p]);
+  } else {
+    constexpr int kUnroll = 16;
+    for (int q0 = 0; q0 < R; q0 += kThreads * kUnroll) {
+      int e[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = q0 + u * kThreads + tid;
-      if (p >= R || (p >= c0 && p < c1)) continue;  // past the end, or this block's own chunk
-      const int k = (e[u] >= 0 && e[u] < E) ? e[u] : E;
-      atomicAdd(p < c0 ? &before[k] : &after[k], 1);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int p = q0 + u * kThreads + tid;
+        e[u] = p < R ? idx[p] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int p = q0 + u * kThreads + tid;
+        if (p < R) count_one(p, e[u]);
+      }
     }
   }
 
@@ -428,12 +458,18 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, i
     const int chunk = nw * kWave;
     const dim3 grid((rows + chunk - 1) / chunk), block(chunk);
     const size_t lds = fused_lds_bytes(nw, E);
-#define EP_LAYOUT_FUSED(NW) \
-  hipLaunchKernelGGL(layout_fused<NW>, grid, block, lds, stream, topk_idx, rows, top_k, E, counts, offsets, slot, src)
-    if (nw >= 16) EP_LAYOUT_FUSED(16);
-    else if (nw >= 8) EP_LAYOUT_FUSED(8);
-    else if (nw >= 4) EP_LAYOUT_FUSED(4);
-    else EP_LAYOUT_FUSED(1);
+#define EP_LAYOUT_FUSED(NW)                                                                         \
+  if (v4)                                                                                           \
+    hipLaunchKernelGGL((layout_fused<NW, true>), grid, block, lds, stream, topk_idx, rows, top_k, E, counts, \
+                       offsets, slot, src);                                                         \
+  else                                                                                              \
+    hipLaunchKernelGGL((layout_fused<NW, false>), grid, block, lds, stream, topk_idx, rows, top_k, E, counts, \
+                       offsets, slot, src)
+    const bool v4 = (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0;
+    if (nw >= 16) { EP_LAYOUT_FUSED(16); }
+    else if (nw >= 8) { EP_LAYOUT_FUSED(8); }
+    else if (nw >= 4) { EP_LAYOUT_FUSED(4); }
+    else { EP_LAYOUT_FUSED(1); }
 #undef EP_LAYOUT_FUSED
     return hipGetLastError();
   }

@@ -20,9 +20,15 @@ def to_dev(a, dtype=None):
     return t.cuda()
 
 
-def gpu_layout(ep, idx, E):
+def gpu_layout(ep, idx, E, misalign=False):
+    """misalign: pass topk_idx 4 bytes past a 16-byte boundary."""
     T, K = idx.shape
-    d_idx = to_dev(idx.astype(np.int32))
+    if misalign:
+        flat = np.concatenate([np.zeros(1, np.int32), idx.astype(np.int32).ravel()])
+        d_idx = to_dev(flat)[1:].view(T, K)
+        assert d_idx.data_ptr() % 16 == 4
+    else:
+        d_idx = to_dev(idx.astype(np.int32))
     counts = torch.full((E,), SENT_I32, dtype=torch.int32, device="cuda")
     offsets = torch.full((E + 1,), SENT_I32, dtype=torch.int32, device="cuda")
     slot = torch.full((T, K), SENT_I32, dtype=torch.int32, device="cuda")

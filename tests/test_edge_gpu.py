@@ -161,3 +161,16 @@ def test_masked_ids_of_every_value(gpu, rows):
     oc, oo, os_, osrc = oracle.dispatch_layout(idx, E)
     assert np.array_equal(host(counts), oc) and np.array_equal(host(offsets), oo)
     assert np.array_equal(host(slot), os_) and np.array_equal(host(src), osrc)
+
+
+@pytest.mark.parametrize("rows", [1030, 9999, 40000])
+def test_layout_unaligned_ids(gpu, rows):
+    """topk_idx only 4-byte aligned: the fused path falls back from 16-byte
+    to 4-byte id loads; same results."""
+    rng = np.random.default_rng(rows + 1)
+    idx = rng.integers(-1, 256, size=(rows, 1)).astype(np.int32)
+    print("case unaligned ids rows", rows, flush=True)
+    counts, offsets, slot, src = gpu_layout(gpu, idx, 256, misalign=True)
+    oc, oo, os_, osrc = oracle.dispatch_layout(idx, 256)
+    assert np.array_equal(host(counts), oc) and np.array_equal(host(offsets), oo)
+    assert np.array_equal(host(slot), os_) and np.array_equal(host(src), osrc)
