@@ -21,12 +21,17 @@ from ._lib import (  # noqa: F401
 )
 from .api import (  # noqa: F401
     Handle,
+    PaddedHandle,
     combine,
     dispatch,
     ep_cast_fp8_e4m3,
     ep_combine,
     ep_dispatch,
     ep_dispatch_layout,
+    ep_dispatch_layout_padded,
     ep_layout_workspace_bytes,
     layout,
+    layout_padded,
+    low_latency_combine,
+    low_latency_dispatch,
 )

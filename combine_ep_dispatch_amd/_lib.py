@@ -24,6 +24,7 @@ EXPORTS = (
     "ep_status_string",
     "ep_layout_workspace_bytes",
     "ep_dispatch_layout",
+    "ep_dispatch_layout_padded",
     "ep_dispatch",
     "ep_combine",
     "ep_cast_fp8_e4m3",
@@ -40,7 +41,7 @@ class EpError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            "libep.so is not built (%s); run `python -m combine_ep_dispatch_amd.build`" % LIB_PATH)
+            "libep.so is not built (%s); run `python combine_ep_dispatch_amd/build.py`" % LIB_PATH)
     # torch first, so that the HIP runtime the library links against is the
     # one torch already holds
     import torch  # noqa: F401
@@ -53,6 +54,8 @@ def _load():
     lib.ep_layout_workspace_bytes.restype = sz
     lib.ep_dispatch_layout.argtypes = [p, i64, i32, i32, p, p, p, p, p, sz, p]
     lib.ep_dispatch_layout.restype = ctypes.c_int
+    lib.ep_dispatch_layout_padded.argtypes = [p, i64, i32, i32, i32, p, p, p, p, sz, p]
+    lib.ep_dispatch_layout_padded.restype = ctypes.c_int
     lib.ep_dispatch.argtypes = [p, i64, i32, i32, p, p, i32, p, p, p, p]
     lib.ep_dispatch.restype = ctypes.c_int
     lib.ep_combine.argtypes = [p, p, p, i64, i32, i32, p, p]

@@ -18,6 +18,8 @@ import torch
 from ._lib import (EP_MAX_EXPERTS, EP_MAX_TOPK, EP_RECV_BF16, EP_RECV_FP8_E4M3_G128, LIB, check)
 
 Handle = namedtuple("Handle", "tokens_per_expert expert_offset slot src_token num_experts")
+# low-latency (padded) handle: expert e owns rows e*capacity .. e*capacity+capacity-1
+PaddedHandle = namedtuple("PaddedHandle", "recv_expert_count slot src_token num_experts capacity")
 
 
 def _stream(stream):
@@ -71,7 +73,29 @@ def ep_dispatch_layout(topk_idx, num_experts, tokens_per_expert, expert_offset, 
         slot.data_ptr(), src_token.data_ptr(), ws_ptr, ws_bytes, _stream(stream)))
 
 
-def ep_dispatch(x, slot, topk_weights, format, recv_x, recv_scale=None, recv_weight=None, stream=None):
+def ep_dispatch_layout_padded(topk_idx, num_experts, capacity, recv_expert_count, slot, src_token,
+                              workspace=None, stream=None):
+    _need(topk_idx, "topk_idx", _I32)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T, K]")
+    T, K = topk_idx.shape
+    E, cap = int(num_experts), int(capacity)
+    _need(recv_expert_count, "recv_expert_count", _I32, (E,))
+    _need(slot, "slot", _I32, (T, K))
+    _need(src_token, "src_token", _I32, (E * cap,))
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8, torch.int32))
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check("ep_dispatch_layout_padded", LIB.ep_dispatch_layout_padded(
+        topk_idx.data_ptr(), T, K, E, cap, recv_expert_count.data_ptr(), slot.data_ptr(), src_token.data_ptr(),
+        ws_ptr, ws_bytes, _stream(stream)))
+
+
+def ep_dispatch(x, slot, topk_weights, format, recv_x, recv_scale=None, recv_weight=None, stream=None,
+                num_rows=None):
+    """num_rows: rows of the receive buffers (T*K by default; E*capacity for
+    a padded slot)."""
     _need(x, "x", _BF16)
     if x.dim() != 2:
         raise ValueError("x must be [T, H]")
@@ -80,19 +104,20 @@ def ep_dispatch(x, slot, topk_weights, format, recv_x, recv_scale=None, recv_wei
     if slot.dim() != 2 or slot.shape[0] != T:
         raise ValueError("slot must be [T, K]")
     K = slot.shape[1]
+    R = T * K if num_rows is None else int(num_rows)
     if topk_weights is not None:
         _need(topk_weights, "topk_weights", _F32, (T, K))
     if format == EP_RECV_FP8_E4M3_G128:
-        _need(recv_x, "recv_x", _U8, (T * K, H))
+        _need(recv_x, "recv_x", _U8, (R, H))
         if H % 128:
             raise ValueError("FP8 dispatch needs hidden % 128 == 0")
-        _need(recv_scale, "recv_scale", _F32, (T * K, H // 128))
+        _need(recv_scale, "recv_scale", _F32, (R, H // 128))
     elif format == EP_RECV_BF16:
-        _need(recv_x, "recv_x", _BF16, (T * K, H))
+        _need(recv_x, "recv_x", _BF16, (R, H))
     else:
         raise ValueError("unknown receive format %r" % (format,))
     if recv_weight is not None:
-        _need(recv_weight, "recv_weight", _F32, (T * K,))
+        _need(recv_weight, "recv_weight", _F32, (R,))
     check("ep_dispatch", LIB.ep_dispatch(
         x.data_ptr(), T, H, K, slot.data_ptr(),
         topk_weights.data_ptr() if topk_weights is not None else None, int(format), recv_x.data_ptr(),
@@ -100,14 +125,16 @@ def ep_dispatch(x, slot, topk_weights, format, recv_x, recv_scale=None, recv_wei
         recv_weight.data_ptr() if recv_weight is not None else None, _stream(stream)))
 
 
-def ep_combine(y, slot, topk_weights, out, stream=None):
+def ep_combine(y, slot, topk_weights, out, stream=None, num_rows=None):
+    """num_rows: rows of y (T*K by default; E*capacity for a padded slot)."""
     _need(slot, "slot", _I32)
     if slot.dim() != 2:
         raise ValueError("slot must be [T, K]")
     T, K = slot.shape
     _need(y, "y", _BF16)
-    if y.dim() != 2 or y.shape[0] < T * K:
-        raise ValueError("y must be [>= T*K, H]")
+    R = T * K if num_rows is None else int(num_rows)
+    if y.dim() != 2 or y.shape[0] != R:
+        raise ValueError("y must be [%d, H]" % R)
     H = y.shape[1]
     _need(topk_weights, "topk_weights", _F32, (T, K))
     _need(out, "out", _BF16, (T, H))
@@ -180,4 +207,57 @@ def combine(y, handle, topk_weights, stream=None):
     T, K = handle.slot.shape
     out = torch.empty((T, y.shape[1]), dtype=torch.bfloat16, device=y.device)
     ep_combine(y, handle.slot, topk_weights.to(torch.float32).contiguous(), out, stream)
+    return out
+
+
+def layout_padded(topk_idx, num_experts, capacity, stream=None):
+    """Low-latency layout with ``capacity`` rows per expert -> PaddedHandle."""
+    if topk_idx.dtype != torch.int32:
+        topk_idx = topk_idx.to(torch.int32)
+    topk_idx = topk_idx.contiguous()
+    T, K = topk_idx.shape
+    E, cap = int(num_experts), int(capacity)
+    dev = topk_idx.device
+    count = torch.empty(E, dtype=torch.int32, device=dev)
+    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+    src = torch.empty(E * cap, dtype=torch.int32, device=dev)
+    nb = ep_layout_workspace_bytes(T, K, E)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    ep_dispatch_layout_padded(topk_idx, E, cap, count, slot, src, ws, stream)
+    return PaddedHandle(count, slot, src, E, cap)
+
+
+def low_latency_dispatch(x, topk_idx, num_max_tokens, num_experts, fp8=True, stream=None):
+    """Decode-time dispatch into a padded buffer, shaped like the pages'
+    ``low_latency_dispatch(hidden_states, topk_idx, num_max_tokens,
+    num_experts)`` ([P4] "使用示例 › 推理解码阶段的应用").
+
+    Returns (recv_x [E, num_max_tokens, H], recv_scale [E, num_max_tokens,
+    H/128] or None, recv_expert_count [E], handle).
+    """
+    h = layout_padded(topk_idx, num_experts, num_max_tokens, stream)
+    T, H = x.shape
+    E, cap = h.num_experts, h.capacity
+    dev = x.device
+    if fp8:
+        recv_x = torch.empty((E * cap, H), dtype=torch.uint8, device=dev)
+        recv_scale = torch.empty((E * cap, H // 128), dtype=torch.float32, device=dev)
+        ep_dispatch(x, h.slot, None, EP_RECV_FP8_E4M3_G128, recv_x, recv_scale, None, stream, num_rows=E * cap)
+        recv_scale = recv_scale.view(E, cap, H // 128)
+    else:
+        recv_x = torch.empty((E * cap, H), dtype=torch.bfloat16, device=dev)
+        recv_scale = None
+        ep_dispatch(x, h.slot, None, EP_RECV_BF16, recv_x, None, None, stream, num_rows=E * cap)
+    return recv_x.view(E, cap, H), recv_scale, h.recv_expert_count, h
+
+
+def low_latency_combine(y, handle, topk_weights, stream=None):
+    """Weighted reduction of padded expert outputs y [E, capacity, H] (bf16)
+    back to token order -> bfloat16 [T, H]."""
+    E, cap = handle.num_experts, handle.capacity
+    H = y.shape[-1]
+    y2 = y.reshape(E * cap, H)
+    T = handle.slot.shape[0]
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    ep_combine(y2, handle.slot, topk_weights.to(torch.float32).contiguous(), out, stream, num_rows=E * cap)
     return out

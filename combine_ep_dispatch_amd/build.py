@@ -1,6 +1,9 @@
 """Build libep.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-    python -m combine_ep_dispatch_amd.build
+    python combine_ep_dispatch_amd/build.py
+
+(Run it as a file, not as a package module: importing the package loads
+libep.so, which is what this script produces.)
 
 Each .hip file is compiled to an object in parallel, then linked.  The
 library links against the HIP runtime that torch loads (torch/lib), so a

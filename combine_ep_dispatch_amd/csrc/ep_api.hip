@@ -62,8 +62,32 @@ EP_API ep_status ep_dispatch_layout(const int32_t* topk_idx, int64_t num_tokens,
   const size_t need = ep::layout_workspace_bytes(rows, num_experts);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
     return EP_ERR_INVALID_ARG;
-  return from_hip(ep::launch_layout(topk_idx, static_cast<int32_t>(rows), top_k, num_experts,
+  return from_hip(ep::launch_layout(topk_idx, static_cast<int32_t>(rows), top_k, num_experts, 0,
                                     tokens_per_expert, expert_offset, slot, src_token, workspace,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+EP_API ep_status ep_dispatch_layout_padded(const int32_t* topk_idx, int64_t num_tokens, int32_t top_k,
+                                           int32_t num_experts, int32_t capacity, int32_t* recv_expert_count,
+                                           int32_t* slot, int32_t* src_token, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  ep_status st = check_common(num_tokens, top_k);
+  if (st != EP_OK) return st;
+  if (num_experts < 1 || capacity < 1) return EP_ERR_INVALID_ARG;
+  if (num_experts > EP_MAX_EXPERTS) return EP_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(num_experts) * capacity >= (int64_t(1) << 31)) return EP_ERR_INVALID_ARG;
+  if (!recv_expert_count || !src_token) return EP_ERR_INVALID_ARG;
+  if (!aligned(recv_expert_count, 4) || !aligned(src_token, 4)) return EP_ERR_INVALID_ARG;
+  const int64_t rows = num_tokens * top_k;
+  if (rows > 0) {
+    if (!topk_idx || !slot) return EP_ERR_INVALID_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(slot, 4)) return EP_ERR_INVALID_ARG;
+  }
+  const size_t need = ep::layout_workspace_bytes(rows, num_experts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return EP_ERR_INVALID_ARG;
+  return from_hip(ep::launch_layout(topk_idx, static_cast<int32_t>(rows), top_k, num_experts, capacity,
+                                    recv_expert_count, nullptr, slot, src_token, workspace,
                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -11,8 +11,10 @@ namespace ep {
 // Layout: chooses the single-workgroup path or the two-kernel multi-block
 // path from the shape.
 size_t layout_workspace_bytes(int64_t rows, int32_t num_experts);
+// capacity == 0: packed layout (counts, offsets, slot, src[T*K]);
+// capacity  > 0: padded layout (counts clamped, offsets unused, src[E*capacity]).
 hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, int32_t num_experts,
-                         int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
+                         int32_t capacity, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
                          void* workspace, hipStream_t stream);
 
 hipError_t launch_dispatch_fp8(const uint16_t* x, int32_t num_tokens, int32_t hidden, int32_t top_k,

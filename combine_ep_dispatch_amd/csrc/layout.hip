@@ -125,9 +125,53 @@ __device__ __forceinline__ void rank_wave_range(const int32_t* __restrict__ idx,
   }
 }
 
+// Row of one entry whose rank among the entries of its key is `within`.
+// Packed layout (cap == 0): row off[k] + within; masked entries (k == E)
+// take the rows after the valid ones with src = -1.  Padded layout
+// (cap > 0): expert e owns rows e*cap .. e*cap+cap-1; entries ranked past
+// the capacity and masked entries get slot -1 and no row.
+__device__ __forceinline__ void write_entry(int p, int k, int within, const int* off, int E, int K, int cap,
+                                            int32_t* __restrict__ slot, int32_t* __restrict__ src) {
+  const bool valid = k < E;
+  const int t = valid ? static_cast<int>(static_cast<uint32_t>(p) / static_cast<uint32_t>(K)) : -1;
+  if (cap == 0) {
+    const int pos = off[k] + within;
+    slot[p] = valid ? pos : -1;
+    src[pos] = t;
+  } else {
+    const bool keep = valid && within < cap;
+    slot[p] = keep ? k * cap + within : -1;
+    if (keep) src[k * cap + within] = t;
+  }
+}
+
+// Counts and offsets from the exclusive scan `off` of the per-key totals;
+// in the padded layout the count is clamped to the capacity and the unused
+// rows of experts part, part+nparts, ... get src = -1 (rows that hold an
+// entry are never touched here, so blocks cannot race).
+__device__ __forceinline__ void write_counts(const int* off, int E, int cap, int part, int nparts,
+                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                             int32_t* __restrict__ src) {
+  const int tid = threadIdx.x, bs = blockDim.x;
+  if (part == 0) {
+    for (int j = tid; j < E; j += bs) {
+      const int total = off[j + 1] - off[j];
+      counts[j] = cap == 0 ? total : min(total, cap);
+    }
+    if (cap == 0)
+      for (int j = tid; j <= E; j += bs) offsets[j] = off[j];
+  }
+  if (cap > 0) {
+    for (int e = part; e < E; e += nparts) {
+      const int used = min(off[e + 1] - off[e], cap);
+      for (int i = used + tid; i < cap; i += bs) src[e * cap + i] = -1;
+    }
+  }
+}
+
 template <int ITERS>
 __global__ __launch_bounds__(kSingleMaxThreads) void layout_single(
-    const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src) {
   extern __shared__ uint64_t lds64[];
   const int tid = threadIdx.x, bs = blockDim.x, nw = bs / kWave, w = tid / kWave;
@@ -157,23 +201,16 @@ __global__ __launch_bounds__(kSingleMaxThreads) void layout_single(
       run += c;
     }
     off[j] = run;
-    if (j < E) counts[j] = run;
   }
   __syncthreads();
   block_exclusive_scan(off, nk, wave_tot);
-  for (int j = tid; j < nk; j += bs) offsets[j] = off[j];
+  write_counts(off, E, cap, 0, 1, counts, offsets, src);
 
   const int lane = tid & (kWave - 1);
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
-    const int p = p_begin + i * kWave + lane;
     const int k = key[i];
-    if (k >= 0) {
-      const int pos = off[k] + cnt[w * nk + k] + rank[i];
-      const bool valid = k < E;
-      slot[p] = valid ? pos : -1;
-      src[pos] = valid ? static_cast<int>(static_cast<uint32_t>(p) / static_cast<uint32_t>(K)) : -1;
-    }
+    if (k >= 0) write_entry(p_begin + i * kWave + lane, k, cnt[w * nk + k] + rank[i], off, E, K, cap, slot, src);
   }
 }
 
@@ -219,7 +256,7 @@ __global__ __launch_bounds__(kMultiThreads) void layout_count(const int32_t* __r
 
 template <int ITERS>
 __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
-    const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t nblocks,
+    const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t nblocks,
     const int32_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ slot, int32_t* __restrict__ src) {
   extern __shared__ int lds[];
@@ -257,22 +294,17 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
     }
     base[j] = before;
     off[j] = total;
-    if (b == 0 && j < E) counts[j] = total;
   }
   __syncthreads();
   block_exclusive_scan(off, nk, wave_tot);
-  if (b == 0)
-    for (int j = tid; j < nk; j += kMultiThreads) offsets[j] = off[j];
+  write_counts(off, E, cap, b, gridDim.x, counts, offsets, src);
 
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
     const int p = b * kChunk + i * kMultiThreads + tid;
     if (p < R) {
-      const bool valid = e[i] >= 0 && e[i] < E;
-      const int k = valid ? e[i] : E;
-      const int pos = off[k] + base[k] + loc[i];
-      slot[p] = valid ? pos : -1;
-      src[pos] = valid ? static_cast<int>(static_cast<uint32_t>(p) / static_cast<uint32_t>(K)) : -1;
+      const int k = (e[i] >= 0 && e[i] < E) ? e[i] : E;
+      write_entry(p, k, base[k] + loc[i], off, E, K, cap, slot, src);
     }
   }
 }
@@ -288,7 +320,7 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
 // trades redundant on-chip work for the second launch and the workspace.
 template <int NW, bool V4>
 __global__ __launch_bounds__(NW * kWave) void layout_fused(
-    const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src) {
   extern __shared__ uint64_t lds64[];
   constexpr int kThreads = NW * kWave;
@@ -371,23 +403,14 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
       cnt[ww * nk + j] = run;
       run += c;
     }
-    const int total = before[j] + run + after[j];
-    after[j] = total;
-    if (blockIdx.x == 0 && j < E) counts[j] = total;
+    after[j] = before[j] + run + after[j];  // total
   }
   __syncthreads();
   block_exclusive_scan(after, nk, wave_tot);
-  if (blockIdx.x == 0)
-    for (int j = tid; j < nk; j += kThreads) offsets[j] = after[j];
+  write_counts(after, E, cap, blockIdx.x, gridDim.x, counts, offsets, src);
 
   const int k = key[0];
-  if (k >= 0) {
-    const int p = p_begin + lane;
-    const int pos = after[k] + before[k] + cnt[w * nk + k] + rank[0];
-    const bool valid = k < E;
-    slot[p] = valid ? pos : -1;
-    src[pos] = valid ? static_cast<int>(static_cast<uint32_t>(p) / static_cast<uint32_t>(K)) : -1;
-  }
+  if (k >= 0) write_entry(p_begin + lane, k, before[k] + cnt[w * nk + k] + rank[0], after, E, K, cap, slot, src);
 }
 
 size_t fused_lds_bytes(int nw, int E) {
@@ -435,7 +458,7 @@ size_t layout_workspace_bytes(int64_t rows, int32_t num_experts) {
 }
 
 hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, int32_t num_experts,
-                         int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
+                         int32_t capacity, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
                          void* workspace, hipStream_t stream) {
   const int E = num_experts, nk = E + 1;
   const LayoutPath path = choose_path(rows);
@@ -445,7 +468,7 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, i
     const size_t lds = single_lds_bytes(nw, E);
     const dim3 grid(1), block(nw * kWave);
 #define EP_LAYOUT_SINGLE(IT)                                                                     \
-  hipLaunchKernelGGL(layout_single<IT>, grid, block, lds, stream, topk_idx, rows, top_k, E, counts, \
+  hipLaunchKernelGGL(layout_single<IT>, grid, block, lds, stream, topk_idx, rows, top_k, E, capacity, counts, \
                      offsets, slot, src)
     if (steps <= 1) EP_LAYOUT_SINGLE(1);
     else if (steps <= 4) EP_LAYOUT_SINGLE(4);
@@ -460,11 +483,11 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, i
     const size_t lds = fused_lds_bytes(nw, E);
 #define EP_LAYOUT_FUSED(NW)                                                                         \
   if (v4)                                                                                           \
-    hipLaunchKernelGGL((layout_fused<NW, true>), grid, block, lds, stream, topk_idx, rows, top_k, E, counts, \
-                       offsets, slot, src);                                                         \
+    hipLaunchKernelGGL((layout_fused<NW, true>), grid, block, lds, stream, topk_idx, rows, top_k, E, capacity, \
+                       counts, offsets, slot, src);                                                 \
   else                                                                                              \
-    hipLaunchKernelGGL((layout_fused<NW, false>), grid, block, lds, stream, topk_idx, rows, top_k, E, counts, \
-                       offsets, slot, src)
+    hipLaunchKernelGGL((layout_fused<NW, false>), grid, block, lds, stream, topk_idx, rows, top_k, E, capacity, \
+                       counts, offsets, slot, src)
     const bool v4 = (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0;
     if (nw >= 16) { EP_LAYOUT_FUSED(16); }
     else if (nw >= 8) { EP_LAYOUT_FUSED(8); }
@@ -481,7 +504,7 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, i
   const dim3 grid(nblocks), block(kMultiThreads);
   hipLaunchKernelGGL(layout_count<kMultiIters>, grid, block, lds_count, stream, topk_idx, rows, E, slot, hist);
   hipLaunchKernelGGL(layout_finalize<kMultiIters>, grid, block, lds_final, stream, topk_idx, rows, top_k, E,
-                     nblocks, hist, counts, offsets, slot, src);
+                     capacity, nblocks, hist, counts, offsets, slot, src);
   return hipGetLastError();
 }
 

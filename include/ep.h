@@ -92,13 +92,42 @@ size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t top_k, int32_t num_
  *                   bytes, 16-byte aligned (may be NULL when that is 0);
  *                   its contents are clobbered.
  * Requirements: T >= 0, 1 <= K <= EP_MAX_TOPK, 1 <= E <= EP_MAX_EXPERTS,
- * T*K < 2^31, int32 arrays 4-byte aligned.  T == 0 writes zero counts and
- * offsets.
+ * T*K <= 2^22, int32 arrays 4-byte aligned.  T == 0 writes zero counts and
+ * offsets.  topk_idx aligned to 16 bytes takes a faster load path.
  */
 ep_status ep_dispatch_layout(const int32_t* topk_idx, int64_t num_tokens, int32_t top_k,
                              int32_t num_experts, int32_t* tokens_per_expert,
                              int32_t* expert_offset, int32_t* slot, int32_t* src_token,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ep_dispatch_layout_padded - the low-latency layout: a fixed capacity of
+ * rows per expert.
+ *
+ * [P4 "使用示例 › 推理解码阶段的应用"]: the low-latency buffer holds
+ * num_max_tokens rows for every expert (num_max_tokens * hidden *
+ * num_experts) and the low-latency dispatch reports recv_expert_count.
+ * Expert e owns receive rows e*capacity .. e*capacity + capacity - 1; an
+ * entry's rank inside its expert is the same stable (t, k) rank as in
+ * ep_dispatch_layout:
+ *   slot[t,k] = e*capacity + rank   if rank < capacity, else -1 (dropped;
+ *               the pages give no overflow rule) and -1 for masked entries
+ *   recv_expert_count[e] = min(#{(t,k) : topk_idx[t,k] == e}, capacity)
+ *   src_token[e*capacity + i] = token of that row for i < recv_expert_count[e],
+ *                               -1 for the unused rows of the expert
+ * With capacity >= T and distinct experts per token nothing is dropped.
+ * ep_dispatch and ep_combine take this slot unchanged; their receive / expert
+ * buffers then have E*capacity rows.
+ *
+ * recv_expert_count int32 [E] out;  slot int32 [T, K] out;
+ * src_token int32 [E*capacity] out;  workspace as for ep_dispatch_layout
+ * (same size function).  Requirements: capacity >= 1, E*capacity < 2^31,
+ * otherwise as for ep_dispatch_layout.
+ */
+ep_status ep_dispatch_layout_padded(const int32_t* topk_idx, int64_t num_tokens, int32_t top_k,
+                                    int32_t num_experts, int32_t capacity, int32_t* recv_expert_count,
+                                    int32_t* slot, int32_t* src_token, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * ep_dispatch - copy every token into its K receive rows.
@@ -118,13 +147,14 @@ ep_status ep_dispatch_layout(const int32_t* topk_idx, int64_t num_tokens, int32_
  * x            bf16 bits [T, H] in, 16-byte aligned
  * slot         int32 [T, K] from ep_dispatch_layout
  * topk_weights float32 [T, K] or NULL (then recv_weight must be NULL)
- * recv_x       [R, H] out: uint8 (FP8) or bf16 bits, 16-byte aligned
- * recv_scale   float32 [R, G] out (FP8 only), 4-byte aligned
- * recv_weight  float32 [R] out or NULL
- * Rows r >= expert_offset[E] (there are none unless entries are masked)
- * are left untouched.  Requirements: H > 0, H % 128 == 0 for FP8,
- * H % 8 == 0 for BF16, 1 <= K <= EP_MAX_TOPK, T*K < 2^31,
- * T*K*H < 2^47 bytes of receive data.
+ * recv_x       [rows, H] out: uint8 (FP8) or bf16 bits, 16-byte aligned;
+ *              rows = T*K for ep_dispatch_layout's slot, E*capacity for
+ *              ep_dispatch_layout_padded's
+ * recv_scale   float32 [rows, G] out (FP8 only), 4-byte aligned
+ * recv_weight  float32 [rows] out or NULL
+ * Rows no entry maps to are left untouched.  Requirements: H > 0,
+ * H % 128 == 0 for FP8, H % 8 == 0 for BF16, 1 <= K <= EP_MAX_TOPK,
+ * T*K <= 2^22, T*H < 2^35.
  */
 ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, int32_t top_k,
                       const int32_t* slot, const float* topk_weights, int32_t format,
@@ -142,11 +172,13 @@ ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, int32_t
  *       acc = RN32(acc + RN32(topk_weights[t,k] * y[r,c]))
  *   out[t,c] = BF16_RNE(acc)
  *
- * y            bf16 bits [>= R, H] in (receive-row order), 16-byte aligned
- * slot         int32 [T, K] from ep_dispatch_layout
+ * y            bf16 bits [rows, H] in (receive-row order; rows as for
+ *              ep_dispatch), 16-byte aligned
+ * slot         int32 [T, K] from ep_dispatch_layout or _padded
  * topk_weights float32 [T, K]
  * out          bf16 bits [T, H] out, 16-byte aligned; must not overlap y
- * Requirements: H > 0, H % 8 == 0, 1 <= K <= EP_MAX_TOPK, T*K < 2^31.
+ * Requirements: H > 0, H % 8 == 0, 1 <= K <= EP_MAX_TOPK, T*K <= 2^22,
+ * T*H < 2^35.
  */
 ep_status ep_combine(const void* y, const int32_t* slot, const float* topk_weights,
                      int64_t num_tokens, int32_t hidden, int32_t top_k, void* out,

@@ -46,6 +46,7 @@ from .codecs import (  # noqa: F401
 )
 from .ep_oracle import (  # noqa: F401
     dispatch_layout,
+    dispatch_layout_padded,
     group_scales,
     quantize_tokens_fp8,
     dispatch_fp8,

@@ -62,6 +62,43 @@ def dispatch_layout(topk_idx, num_experts):
             slot.reshape(T, K).astype(np.int32), src.astype(np.int32))
 
 
+def dispatch_layout_padded(topk_idx, num_experts, capacity):
+    """Low-latency (padded) layout: expert e owns rows e*capacity ..
+    (e+1)*capacity - 1 of the receive buffer.
+
+    [P4 "推理解码阶段的应用"]: the low-latency buffer is sized
+    num_max_tokens * hidden * num_experts, i.e. a fixed per-expert capacity
+    of num_max_tokens rows, and the low-latency dispatch reports the number
+    of tokens each expert received (recv_expert_count).  Reading taken: the
+    entry's rank inside its expert is the same stable (t, k) rank as in
+    ``dispatch_layout``; its row is e*capacity + rank.  The pages give no
+    overflow rule; here an entry whose rank is >= capacity is dropped
+    (slot -1, skipped by dispatch and combine) and recv_expert_count[e] =
+    min(count, capacity).  With capacity >= T and distinct experts per token
+    nothing is ever dropped.
+
+    Returns
+      recv_count int32[E]          rows used in each expert's block
+      slot       int32[T, K]       receive row of (t, k), or -1
+      src        int32[E*capacity] token of each used row; -1 elsewhere
+    """
+    idx = np.asarray(topk_idx)
+    T, K = idx.shape
+    E, cap = int(num_experts), int(capacity)
+    counts, offsets, slot_packed, _ = dispatch_layout(idx, E)
+    flat = idx.reshape(-1).astype(np.int64)
+    sp = slot_packed.reshape(-1).astype(np.int64)
+    valid = sp >= 0
+    rank = np.where(valid, sp - offsets[np.clip(flat, 0, E - 1)], 0)
+    keep = valid & (rank < cap)
+    slot = np.where(keep, np.clip(flat, 0, E - 1) * cap + rank, -1)
+    src = np.full(E * cap, -1, dtype=np.int64)
+    pos = np.flatnonzero(keep)
+    src[slot[pos]] = pos // K
+    recv_count = np.minimum(counts.astype(np.int64), cap)
+    return recv_count.astype(np.int32), slot.reshape(T, K).astype(np.int32), src.astype(np.int32)
+
+
 def group_scales(xf):
     """One FP32 scale per (token, 128-channel group).
 

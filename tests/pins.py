@@ -163,3 +163,24 @@ def brute_layout(topk_idx, E):
     for (t, k, e) in valid:
         src[slot[t][k]] = t
     return counts, offsets, slot, src
+
+
+def brute_layout_padded(topk_idx, E, cap):
+    """Padded layout by counting: rank = earlier (t, k) entries with the
+    same expert; kept when rank < cap, at row e*cap + rank."""
+    T = len(topk_idx)
+    K = len(topk_idx[0]) if T else 0
+    slot = [[-1] * K for _ in range(T)]
+    seen = [0] * E
+    src = [-1] * (E * cap)
+    for t in range(T):
+        for k in range(K):
+            e = int(topk_idx[t][k])
+            if not 0 <= e < E:
+                continue
+            r = seen[e]
+            seen[e] += 1
+            if r < cap:
+                slot[t][k] = e * cap + r
+                src[e * cap + r] = t
+    return [min(c, cap) for c in seen], slot, src

@@ -110,3 +110,18 @@ def test_product_package_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in re.sub(r"#.*|//.*", "", text), f
+
+
+def test_padded_layout_rejects_bad_arguments(lib):
+    P = lib.LIB.ep_dispatch_layout_padded
+
+    def call(T=4, K=2, E=8, cap=16, cnt=FAKE, s=FAKE, r=FAKE, idx=FAKE):
+        return P(idx, T, K, E, cap, cnt, s, r, None, 0, None)
+
+    assert call(cap=0) == lib.EP_ERR_INVALID_ARG
+    assert call(E=1024, cap=1 << 21) == lib.EP_ERR_INVALID_ARG  # E*cap >= 2**31
+    assert call(cnt=None) == lib.EP_ERR_INVALID_ARG
+    assert call(r=None) == lib.EP_ERR_INVALID_ARG
+    assert call(s=None) == lib.EP_ERR_INVALID_ARG
+    assert call(E=2000) == lib.EP_ERR_UNSUPPORTED
+    assert call(T=8200, K=8, E=256) == lib.EP_ERR_INVALID_ARG  # needs a workspace

@@ -136,3 +136,37 @@ def test_skew_has_hot_experts_and_holes_variant_has_empty_experts():
     assert c.max() > 1000 and c.min() >= 0
     c2 = dispatch_layout(make_workload("skew", seed=0, holes_frac=0.25).topk_idx, 256)[0]
     assert (c2 == 0).sum() == 64
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.integers(1, 6).flatmap(lambda E: st.tuples(
+    st.just(E), st.integers(1, 5),
+    st.integers(0, 10).flatmap(lambda T: st.integers(1, 3).flatmap(lambda K: st.lists(
+        st.lists(st.integers(-2, E), min_size=K, max_size=K), min_size=T, max_size=T).map(
+            lambda rows: np.array(rows, dtype=np.int32).reshape(T, K)))))))
+def test_padded_matches_brute_force(args):
+    from oracle import dispatch_layout_padded
+    from tests.pins import brute_layout_padded
+
+    E, cap, idx = args
+    rc, slot, src = dispatch_layout_padded(idx, E, cap)
+    bc, bs, bsrc = brute_layout_padded(idx.tolist(), E, cap)
+    assert rc.tolist() == bc
+    assert slot.tolist() == (bs if idx.shape[0] else [])
+    assert src.tolist() == bsrc
+
+
+def test_padded_with_enough_capacity_is_the_packed_layout_rebased():
+    """Special case: capacity >= every count drops nothing, and each row is
+    the packed row moved from offsets[e] to e*capacity."""
+    from oracle import dispatch_layout_padded
+
+    wl = make_workload("decode", seed=0)
+    counts, offsets, slot, src = dispatch_layout(wl.topk_idx, wl.E)
+    rc, pslot, psrc = dispatch_layout_padded(wl.topk_idx, wl.E, wl.T)
+    assert np.array_equal(rc, counts)
+    e = wl.topk_idx
+    assert np.array_equal(pslot, e * wl.T + (slot - offsets[e]))
+    for ex in range(wl.E):
+        assert np.array_equal(psrc[ex * wl.T: ex * wl.T + counts[ex]], src[offsets[ex]:offsets[ex + 1]])
+        assert np.all(psrc[ex * wl.T + counts[ex]:(ex + 1) * wl.T] == -1)
