@@ -53,4 +53,7 @@ from .ep_oracle import (  # noqa: F401
     dispatch_bf16,
     combine,
     dequantize_rows,
+    dispatch_backward,
+    combine_backward,
+    pairwise_sum_f32,
 )

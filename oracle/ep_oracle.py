@@ -240,3 +240,78 @@ def dequantize_rows(recv, recv_scale):
     qf = e4m3_to_f32(recv).reshape(R, H // GROUP, GROUP)
     y = (qf * np.asarray(recv_scale, dtype=np.float32)[:, :, None]).astype(np.float32)
     return f32_to_bf16_rne(y.reshape(R, H))
+
+
+# ---- backward helpers --------------------------------------------------------
+# [P5 "典型工作流程"]: besides combine, the library offers backward helper
+# functions for training.  The pages give no arithmetic for them; the
+# readings below follow the forward definitions.
+
+VEC = 8  # channels per partial sum of a row dot product
+
+
+def dispatch_backward(grad_recv_bits, slot):
+    """Gradient of dispatch w.r.t. x: the K copies' gradients summed.
+
+    Dispatch copies token t into K rows, so d x[t] = sum_k d recv[slot[t,k]]
+    (the FP8 cast is passed straight through).  Same arithmetic as combine
+    with unit weights: binary32, ascending k, from +0.0, BF16 RNE.
+    """
+    slot = np.asarray(slot)
+    return combine(grad_recv_bits, slot, np.ones(slot.shape, dtype=np.float32))
+
+
+def pairwise_sum_f32(parts):
+    """Sum the last axis of float32 ``parts`` as a complete binary tree of
+    adjacent pairs (leaf i meets leaf i^1 first, then pairs of pairs, ...),
+    after padding the axis to a power of two with -0.0 (x + -0.0 == x for
+    every x, so padding never changes a value)."""
+    a = np.asarray(parts, dtype=np.float32)
+    n = a.shape[-1]
+    m = 1
+    while m < n:
+        m *= 2
+    if m > n:
+        pad = np.full(a.shape[:-1] + (m - n,), -0.0, dtype=np.float32)
+        a = np.concatenate([a, pad], axis=-1)
+    while a.shape[-1] > 1:
+        a = a.reshape(a.shape[:-1] + (a.shape[-1] // 2, 2))
+        a = (a[..., 0] + a[..., 1]).astype(np.float32)
+    return a[..., 0]
+
+
+def combine_backward(grad_out_bits, y_bits, slot, topk_weights, num_rows=None):
+    """Gradients of combine w.r.t. the expert outputs y and the weights.
+
+    combine computes out[t] = sum_k w[t,k] * y[slot[t,k]], so
+      grad_y[slot[t,k], c] = BF16_RNE(RN32(w[t,k] * grad_out[t,c]))
+      grad_w[t,k]          = sum_c grad_out[t,c] * y[slot[t,k], c]
+    The dot product is given a fixed order so that it is reproducible: each
+    8-channel vector's products are added in channel order into +0.0, then
+    the H/8 vector sums are added as a pairwise tree (``pairwise_sum_f32``).
+    Masked entries (slot -1) get grad_w = +0.0 and no grad_y row; grad_y
+    rows no entry maps to are returned as zeros (the GPU leaves them
+    untouched).
+
+    Returns (grad_y uint16[num_rows, H], grad_w float32[T, K]).
+    """
+    g = bf16_bits_to_f32(np.asarray(grad_out_bits, dtype=np.uint16))
+    yb = np.asarray(y_bits, dtype=np.uint16)
+    slot = np.asarray(slot)
+    w = np.asarray(topk_weights, dtype=np.float32)
+    T, K = slot.shape
+    H = g.shape[1]
+    R = T * K if num_rows is None else int(num_rows)
+    grad_y = np.zeros((R, H), dtype=np.uint16)
+    grad_w = np.zeros((T, K), dtype=np.float32)
+    for k in range(K):
+        r = slot[:, k].astype(np.int64)
+        m = r >= 0
+        gy = (w[m, k][:, None] * g[m]).astype(np.float32)
+        grad_y[r[m]] = f32_to_bf16_rne(gy)
+        prod = (g[m] * bf16_bits_to_f32(yb[r[m]])).astype(np.float32).reshape(-1, H // VEC, VEC)
+        part = np.zeros(prod.shape[:2], dtype=np.float32)
+        for i in range(VEC):
+            part = (part + prod[:, :, i]).astype(np.float32)
+        grad_w[m, k] = pairwise_sum_f32(part)
+    return grad_y, grad_w
