@@ -36,6 +36,15 @@ COMBINE_SOURCES = ["combine_ep_dispatch_amd/csrc/combine.hip", "combine_ep_dispa
 TRAFFIC_FILE = os.path.join(PROFILES, "combine_prefill_4096x7168_top8_traffic.txt")
 
 
+def backward_bytes(T, H, K):
+    """Algorithmic bytes of the backward helpers: dispatch_backward reads the
+    K row gradients and writes the token gradient; combine_backward reads
+    grad_out and the K expert rows and writes K row gradients and K weights."""
+    dispatch_bwd = 2 * T * K * H + 4 * T * K + 2 * T * H
+    combine_bwd = 2 * T * H + 2 * T * K * H + 8 * T * K + 2 * T * K * H + 4 * T * K
+    return dispatch_bwd, combine_bwd
+
+
 def alg_bytes(T, H, E, K, fp8=True):
     """Bytes each kernel must move (reads + writes), all K copies counted."""
     layout = 12 * T * K + 8 * E + 4  # idx in; slot, src out; counts, offsets out
@@ -114,6 +123,21 @@ class Setup:
         self.dispatch()
         self.combine()
 
+    def backward_buffers(self, torch):
+        T, H, K = self.wl.T, self.wl.H, self.wl.K
+        self.grad_out = torch.randn((T, H), device="cuda").to(torch.bfloat16)
+        self.grad_x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        self.grad_y = torch.empty((self.rows, H), dtype=torch.bfloat16, device="cuda")
+        self.grad_w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+
+    def dispatch_backward(self):
+        # the expert-output tensor stands in for the receive-row gradients
+        self.ep.ep_dispatch_backward(self.y, self.slot, self.grad_x, num_rows=self.rows)
+
+    def combine_backward(self):
+        self.ep.ep_combine_backward(self.grad_out, self.y, self.slot, self.w, self.grad_y, self.grad_w,
+                                    num_rows=self.rows)
+
 
 def time_steps(torch, s, steps, warmup):
     """K steps bracketed by synchronisation, timed with HIP events on the
@@ -168,6 +192,21 @@ def time_graph(torch, s, replays):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e3 / replays
+
+
+def time_calls(torch, fn, reps, warmup=3):
+    """Mean µs of one call, HIP events around each call on the launch stream."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) * 1e3 / reps
 
 
 def read_traffic():
@@ -234,6 +273,11 @@ def profile_pass(ep, torch, workload="prefill"):
     s = Setup(ep, torch, workload, 0)
     for _ in range(5):
         s.step()
+    if s.wl.fp8:
+        s.backward_buffers(torch)
+        for _ in range(3):
+            s.dispatch_backward()
+            s.combine_backward()
     torch.cuda.synchronize()
     print("profile pass done", flush=True)
 
@@ -356,6 +400,10 @@ def main():
     total_b = lay_b + dis_b + com_b
     gbs = total_b / (us_step * 1e-6) / 1e9
     graph_us = time_graph(torch, s, 50)
+    s.backward_buffers(torch)
+    db_b, cb_b = backward_bytes(s.wl.T, s.wl.H, s.wl.K)
+    db_us = time_calls(torch, s.dispatch_backward, 30)
+    cb_us = time_calls(torch, s.combine_backward, 30)
 
     d = Setup(ep, torch, "decode", 0)
     d_us, d_per, _ = time_steps(torch, d, 200, 10)
@@ -394,6 +442,9 @@ def main():
                              "kernel_us": {k: round(v, 2) for k, v in d_per.items()},
                              "low_latency_padded_128": {"stream": round(dl_us, 2), "graph": round(dl_graph, 2),
                                                         "kernel_us": {k: round(v, 2) for k, v in dl_per.items()}}},
+        "backward_us": {"dispatch_backward": round(db_us, 2), "combine_backward": round(cb_us, 2),
+                        "dispatch_backward_GBs": round(db_b / db_us / 1e3, 1),
+                        "combine_backward_GBs": round(cb_b / cb_us / 1e3, 1)},
         "roofline": {"bound": "hbm", "kernel": "combine", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic},

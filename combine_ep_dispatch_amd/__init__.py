@@ -23,9 +23,13 @@ from .api import (  # noqa: F401
     Handle,
     PaddedHandle,
     combine,
+    combine_backward,
     dispatch,
+    dispatch_backward,
     ep_cast_fp8_e4m3,
     ep_combine,
+    ep_combine_backward,
+    ep_dispatch_backward,
     ep_dispatch,
     ep_dispatch_layout,
     ep_dispatch_layout_padded,

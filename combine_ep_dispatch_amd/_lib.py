@@ -27,6 +27,8 @@ EXPORTS = (
     "ep_dispatch_layout_padded",
     "ep_dispatch",
     "ep_combine",
+    "ep_dispatch_backward",
+    "ep_combine_backward",
     "ep_cast_fp8_e4m3",
 )
 
@@ -60,6 +62,10 @@ def _load():
     lib.ep_dispatch.restype = ctypes.c_int
     lib.ep_combine.argtypes = [p, p, p, i64, i32, i32, p, p]
     lib.ep_combine.restype = ctypes.c_int
+    lib.ep_dispatch_backward.argtypes = [p, p, i64, i32, i32, p, p]
+    lib.ep_dispatch_backward.restype = ctypes.c_int
+    lib.ep_combine_backward.argtypes = [p, p, p, p, i64, i32, i32, p, p, p]
+    lib.ep_combine_backward.restype = ctypes.c_int
     lib.ep_cast_fp8_e4m3.argtypes = [p, p, i64, p]
     lib.ep_cast_fp8_e4m3.restype = ctypes.c_int
     return lib

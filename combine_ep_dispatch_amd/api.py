@@ -142,6 +142,44 @@ def ep_combine(y, slot, topk_weights, out, stream=None, num_rows=None):
                                        out.data_ptr(), _stream(stream)))
 
 
+def ep_dispatch_backward(grad_recv, slot, grad_x, stream=None, num_rows=None):
+    """grad_x [T, H] = sum over k of grad_recv[slot[t, k]] (bf16)."""
+    _need(slot, "slot", _I32)
+    if slot.dim() != 2:
+        raise ValueError("slot must be [T, K]")
+    T, K = slot.shape
+    _need(grad_recv, "grad_recv", _BF16)
+    R = T * K if num_rows is None else int(num_rows)
+    if grad_recv.dim() != 2 or grad_recv.shape[0] != R:
+        raise ValueError("grad_recv must be [%d, H]" % R)
+    H = grad_recv.shape[1]
+    _need(grad_x, "grad_x", _BF16, (T, H))
+    check("ep_dispatch_backward", LIB.ep_dispatch_backward(grad_recv.data_ptr(), slot.data_ptr(), T, H, K,
+                                                           grad_x.data_ptr(), _stream(stream)))
+
+
+def ep_combine_backward(grad_out, y, slot, topk_weights, grad_y, grad_w=None, stream=None, num_rows=None):
+    """grad_y rows = w * grad_out (bf16); grad_w [T, K] = row dot products
+    (float32), or skipped when grad_w is None (y may then be None)."""
+    _need(slot, "slot", _I32)
+    if slot.dim() != 2:
+        raise ValueError("slot must be [T, K]")
+    T, K = slot.shape
+    _need(grad_out, "grad_out", _BF16)
+    if grad_out.dim() != 2 or grad_out.shape[0] != T:
+        raise ValueError("grad_out must be [T, H]")
+    H = grad_out.shape[1]
+    R = T * K if num_rows is None else int(num_rows)
+    _need(topk_weights, "topk_weights", _F32, (T, K))
+    _need(grad_y, "grad_y", _BF16, (R, H))
+    if grad_w is not None:
+        _need(y, "y", _BF16, (R, H))
+        _need(grad_w, "grad_w", _F32, (T, K))
+    check("ep_combine_backward", LIB.ep_combine_backward(
+        grad_out.data_ptr(), y.data_ptr() if y is not None else None, slot.data_ptr(), topk_weights.data_ptr(),
+        T, H, K, grad_y.data_ptr(), grad_w.data_ptr() if grad_w is not None else None, _stream(stream)))
+
+
 def ep_cast_fp8_e4m3(inp, out, stream=None):
     _need(inp, "in", _F32)
     _need(out, "out", _U8, tuple(inp.shape))
@@ -261,3 +299,24 @@ def low_latency_combine(y, handle, topk_weights, stream=None):
     out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
     ep_combine(y2, handle.slot, topk_weights.to(torch.float32).contiguous(), out, stream, num_rows=E * cap)
     return out
+
+
+def dispatch_backward(grad_recv, handle, stream=None):
+    """Gradient of dispatch w.r.t. x: the K copies' gradients summed -> bf16 [T, H]."""
+    T, K = handle.slot.shape
+    R = grad_recv.shape[0]
+    out = torch.empty((T, grad_recv.shape[1]), dtype=torch.bfloat16, device=grad_recv.device)
+    ep_dispatch_backward(grad_recv, handle.slot, out, stream, num_rows=R)
+    return out
+
+
+def combine_backward(grad_out, y, handle, topk_weights, stream=None):
+    """Gradients of combine -> (grad_y bf16 [rows, H], grad_w float32 [T, K]).
+    Rows no entry maps to are zero-filled first (a torch fill)."""
+    T, K = handle.slot.shape
+    R, H = y.shape
+    grad_y = torch.zeros((R, H), dtype=torch.bfloat16, device=y.device)
+    grad_w = torch.empty((T, K), dtype=torch.float32, device=y.device)
+    ep_combine_backward(grad_out, y, handle.slot, topk_weights.to(torch.float32).contiguous(), grad_y, grad_w,
+                        stream, num_rows=R)
+    return grad_y, grad_w

@@ -6,6 +6,9 @@
 // Arithmetic (not fixed by the pages): binary32, k ascending, each product
 // rounded before it is added (__fmul_rn / __fadd_rn, so the compiler cannot
 // fuse them), starting from +0.0, one BF16 round-to-nearest-even at the end.
+// With no weights (w == nullptr) every weight is 1 (the product is exact):
+// that is the backward of dispatch, which sums the gradients of a token's K
+// copies ([P5 "典型工作流程"] lists backward helpers beside combine).
 //
 // gfx950 design: bound by HBM reads (K gathered rows per output row).  Work
 // item = (token, 8 channels): the K row indices and weights are loaded
@@ -37,7 +40,7 @@ __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y,
   for (int j = 0; j < KC; ++j) {
     const bool in = k0 + j < K;
     r[j] = in ? srow[k0 + j] : -1;
-    wk[j] = in ? wrow[k0 + j] : 0.0f;
+    wk[j] = in ? (wrow != nullptr ? wrow[k0 + j] : 1.0f) : 0.0f;  // no weights: unit weights
   }
   u32x4 d[KC];
 #pragma unroll
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
   const uint32_t t = item / vpt;
   const uint32_t v = item - t * vpt;  // 8-channel vector within the token
   const int32_t* srow = slot + static_cast<size_t>(t) * K;
-  const float* wrow = w + static_cast<size_t>(t) * K;
+  const float* wrow = w != nullptr ? w + static_cast<size_t>(t) * K : nullptr;
 
   float acc[8];
 #pragma unroll

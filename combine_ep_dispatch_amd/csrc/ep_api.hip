@@ -134,6 +134,39 @@ EP_API ep_status ep_combine(const void* y, const int32_t* slot, const float* top
                                      static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
 }
 
+EP_API ep_status ep_dispatch_backward(const void* grad_recv, const int32_t* slot, int64_t num_tokens,
+                                      int32_t hidden, int32_t top_k, void* grad_x, void* stream) {
+  ep_status st = check_common(num_tokens, top_k);
+  if (st != EP_OK) return st;
+  if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARG;
+  if (num_tokens * hidden >= (int64_t(1) << 35)) return EP_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return EP_OK;
+  if (!grad_recv || !slot || !grad_x) return EP_ERR_INVALID_ARG;
+  if (!aligned(grad_recv, 16) || !aligned(grad_x, 16) || !aligned(slot, 4)) return EP_ERR_INVALID_ARG;
+  return from_hip(ep::launch_combine(static_cast<const uint16_t*>(grad_recv), slot, nullptr,
+                                     static_cast<int32_t>(num_tokens), hidden, top_k,
+                                     static_cast<uint16_t*>(grad_x), static_cast<hipStream_t>(stream)));
+}
+
+EP_API ep_status ep_combine_backward(const void* grad_out, const void* y, const int32_t* slot,
+                                     const float* topk_weights, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                                     void* grad_y, float* grad_w, void* stream) {
+  ep_status st = check_common(num_tokens, top_k);
+  if (st != EP_OK) return st;
+  if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARG;
+  if (hidden > 8192) return EP_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return EP_OK;
+  if (!grad_out || !slot || !topk_weights || !grad_y) return EP_ERR_INVALID_ARG;
+  if (grad_w != nullptr && y == nullptr) return EP_ERR_INVALID_ARG;
+  if (!aligned(grad_out, 16) || !aligned(grad_y, 16) || !aligned(slot, 4) || !aligned(topk_weights, 4))
+    return EP_ERR_INVALID_ARG;
+  if (grad_w != nullptr && (!aligned(y, 16) || !aligned(grad_w, 4))) return EP_ERR_INVALID_ARG;
+  return from_hip(ep::launch_combine_backward(
+      static_cast<const uint16_t*>(grad_out), static_cast<const uint16_t*>(y), slot, topk_weights,
+      static_cast<int32_t>(num_tokens), hidden, top_k, static_cast<uint16_t*>(grad_y), grad_w,
+      static_cast<hipStream_t>(stream)));
+}
+
 EP_API ep_status ep_cast_fp8_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
   if (n < 0) return EP_ERR_INVALID_ARG;
   if (n >= (int64_t(1) << 40)) return EP_ERR_UNSUPPORTED;

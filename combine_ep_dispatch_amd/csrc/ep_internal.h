@@ -25,9 +25,15 @@ hipError_t launch_dispatch_bf16(const uint16_t* x, int32_t num_tokens, int32_t h
                                 const int32_t* slot, const float* topk_weights, uint16_t* recv,
                                 float* recv_weight, hipStream_t stream);
 
+// topk_weights == nullptr: unit weights (the backward of dispatch)
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* topk_weights,
                           int32_t num_tokens, int32_t hidden, int32_t top_k, uint16_t* out,
                           hipStream_t stream);
+
+// grad_w may be null (then y is not read)
+hipError_t launch_combine_backward(const uint16_t* grad_out, const uint16_t* y, const int32_t* slot,
+                                   const float* w, int32_t num_tokens, int32_t hidden, int32_t top_k,
+                                   uint16_t* grad_y, float* grad_w, hipStream_t stream);
 
 hipError_t launch_cast_fp8(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 

@@ -185,6 +185,41 @@ ep_status ep_combine(const void* y, const int32_t* slot, const float* topk_weigh
                      void* stream);
 
 /*
+ * ep_dispatch_backward - gradient of dispatch w.r.t. the tokens.
+ *
+ * [P5 "典型工作流程"] lists backward helpers beside combine; the pages give
+ * no arithmetic.  Dispatch copies token t into K rows, so its gradient sums
+ * the K rows' gradients (an FP8 cast is passed straight through).  Same
+ * arithmetic as ep_combine with every weight 1:
+ *   grad_x[t,c] = BF16_RNE(+0.0 + grad_recv[slot[t,0],c] + ... ), binary32,
+ *   ascending k, masked entries skipped.
+ * grad_recv bf16 [rows, H] in; slot int32 [T, K]; grad_x bf16 [T, H] out.
+ * Requirements as for ep_combine.
+ */
+ep_status ep_dispatch_backward(const void* grad_recv, const int32_t* slot, int64_t num_tokens,
+                               int32_t hidden, int32_t top_k, void* grad_x, void* stream);
+
+/*
+ * ep_combine_backward - gradients of combine w.r.t. the expert outputs y
+ * and the routing weights ([P5 "典型工作流程"], backward helpers):
+ *   grad_y[slot[t,k], c] = BF16_RNE(RN32(topk_weights[t,k] * grad_out[t,c]))
+ *   grad_w[t,k] = sum_c grad_out[t,c] * y[slot[t,k], c]      (binary32)
+ * The dot product has a fixed order: the 8 products of each 8-channel
+ * vector are added in channel order into +0.0, then the H/8 vector sums are
+ * added as a complete binary tree of adjacent pairs padded with -0.0.
+ * Masked entries get grad_w = +0.0 and no grad_y row; other grad_y rows are
+ * left untouched.
+ * grad_out bf16 [T, H]; y bf16 [rows, H] (may be NULL when grad_w is NULL);
+ * slot int32 [T, K]; topk_weights float32 [T, K]; grad_y bf16 [rows, H]
+ * out; grad_w float32 [T, K] out or NULL.
+ * Requirements: H % 8 == 0, H <= 8192 (one workgroup per token), otherwise
+ * as for ep_combine.
+ */
+ep_status ep_combine_backward(const void* grad_out, const void* y, const int32_t* slot,
+                              const float* topk_weights, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                              void* grad_y, float* grad_w, void* stream);
+
+/*
  * ep_cast_fp8_e4m3 - the binary32 -> E4M3FN conversion ep_dispatch uses,
  * applied elementwise: out[i] = E4M3FN_RNE_satfinite(in[i]).  Magnitudes
  * beyond 448 saturate to +-448; NaN inputs are outside the contract.
