@@ -129,7 +129,8 @@ __device__ __forceinline__ void rank_wave_range(const int32_t* __restrict__ idx,
 // Packed layout (cap == 0): row off[k] + within; masked entries (k == E)
 // take the rows after the valid ones with src = -1.  Padded layout
 // (cap > 0): expert e owns rows e*cap .. e*cap+cap-1; entries ranked past
-// the capacity and masked entries get slot -1 and no row.
+// the capacity and masked entries get slot -1 and no row, and the unused
+// rows of an expert's block are not written.
 __device__ __forceinline__ void write_entry(int p, int k, int within, const int* off, int E, int K, int cap,
                                             int32_t* __restrict__ slot, int32_t* __restrict__ src) {
   const bool valid = k < E;
@@ -145,28 +146,19 @@ __device__ __forceinline__ void write_entry(int p, int k, int within, const int*
   }
 }
 
-// Counts and offsets from the exclusive scan `off` of the per-key totals;
-// in the padded layout the count is clamped to the capacity and the unused
-// rows of experts part, part+nparts, ... get src = -1 (rows that hold an
-// entry are never touched here, so blocks cannot race).
-__device__ __forceinline__ void write_counts(const int* off, int E, int cap, int part, int nparts,
-                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                             int32_t* __restrict__ src) {
+// Counts and offsets from the exclusive scan `off` of the per-key totals
+// (written by one workgroup); in the padded layout the count is clamped to
+// the capacity and there are no offsets.
+__device__ __forceinline__ void write_counts(const int* off, int E, int cap, int part, int32_t* __restrict__ counts,
+                                             int32_t* __restrict__ offsets) {
+  if (part != 0) return;
   const int tid = threadIdx.x, bs = blockDim.x;
-  if (part == 0) {
-    for (int j = tid; j < E; j += bs) {
-      const int total = off[j + 1] - off[j];
-      counts[j] = cap == 0 ? total : min(total, cap);
-    }
-    if (cap == 0)
-      for (int j = tid; j <= E; j += bs) offsets[j] = off[j];
+  for (int j = tid; j < E; j += bs) {
+    const int total = off[j + 1] - off[j];
+    counts[j] = cap == 0 ? total : min(total, cap);
   }
-  if (cap > 0) {
-    for (int e = part; e < E; e += nparts) {
-      const int used = min(off[e + 1] - off[e], cap);
-      for (int i = used + tid; i < cap; i += bs) src[e * cap + i] = -1;
-    }
-  }
+  if (cap == 0)
+    for (int j = tid; j <= E; j += bs) offsets[j] = off[j];
 }
 
 template <int ITERS>
@@ -204,7 +196,7 @@ __global__ __launch_bounds__(kSingleMaxThreads) void layout_single(
   }
   __syncthreads();
   block_exclusive_scan(off, nk, wave_tot);
-  write_counts(off, E, cap, 0, 1, counts, offsets, src);
+  write_counts(off, E, cap, 0, counts, offsets);
 
   const int lane = tid & (kWave - 1);
 #pragma unroll
@@ -297,7 +289,7 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
   }
   __syncthreads();
   block_exclusive_scan(off, nk, wave_tot);
-  write_counts(off, E, cap, b, gridDim.x, counts, offsets, src);
+  write_counts(off, E, cap, b, counts, offsets);
 
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
@@ -407,7 +399,7 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
   }
   __syncthreads();
   block_exclusive_scan(after, nk, wave_tot);
-  write_counts(after, E, cap, blockIdx.x, gridDim.x, counts, offsets, src);
+  write_counts(after, E, cap, blockIdx.x, counts, offsets);
 
   const int k = key[0];
   if (k >= 0) write_entry(p_begin + lane, k, before[k] + cnt[w * nk + k] + rank[0], after, E, K, cap, slot, src);

@@ -113,8 +113,8 @@ ep_status ep_dispatch_layout(const int32_t* topk_idx, int64_t num_tokens, int32_
  *   slot[t,k] = e*capacity + rank   if rank < capacity, else -1 (dropped;
  *               the pages give no overflow rule) and -1 for masked entries
  *   recv_expert_count[e] = min(#{(t,k) : topk_idx[t,k] == e}, capacity)
- *   src_token[e*capacity + i] = token of that row for i < recv_expert_count[e],
- *                               -1 for the unused rows of the expert
+ *   src_token[e*capacity + i] = token of that row for i < recv_expert_count[e];
+ *                               the unused rows of an expert are not written
  * With capacity >= T and distinct experts per token nothing is dropped.
  * ep_dispatch and ep_combine take this slot unchanged; their receive / expert
  * buffers then have E*capacity rows.

@@ -80,7 +80,8 @@ def dispatch_layout_padded(topk_idx, num_experts, capacity):
     Returns
       recv_count int32[E]          rows used in each expert's block
       slot       int32[T, K]       receive row of (t, k), or -1
-      src        int32[E*capacity] token of each used row; -1 elsewhere
+      src        int32[E*capacity] token of each used row; -1 elsewhere (the
+                 GPU path leaves unused rows untouched; compare used rows)
     """
     idx = np.asarray(topk_idx)
     T, K = idx.shape

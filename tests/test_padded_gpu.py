@@ -29,7 +29,10 @@ def check_layout(ep, idx, E, cap):
     oc, os_, osrc = oracle.dispatch_layout_padded(idx, E, cap)
     assert np.array_equal(host(count), oc)
     assert np.array_equal(host(slot), os_)
-    assert np.array_equal(host(src), osrc)
+    used = (np.arange(cap)[None, :] < oc[:, None]).ravel()
+    hs = host(src)
+    assert np.array_equal(hs[used], osrc[used])
+    assert np.all(hs[~used] == SENT_I32)  # unused rows are not written
     return slot, os_
 
 
