@@ -360,12 +360,35 @@ def summarize_profile(dirname):
         print(open(os.path.join(PROFILES, p)).read())
 
 
+def other_workload(ep, torch, args):
+    """One JSON line for a non-headline configuration (same timing method)."""
+    s = Setup(ep, torch, args.workload, 0)
+    lay_b, dis_b, com_b = s.bytes
+    us_step, per_kernel, _ = time_steps(torch, s, args.steps, args.warmup)
+    graph_us = time_graph(torch, s, 20 if s.wl.T > 8192 else 200)
+    total = lay_b + dis_b + com_b
+    wl = s.wl
+    rec = {"metric": "step µs and algorithmic GB/s", "workload": args.workload,
+           "config": {"tokens": wl.T, "hidden": wl.H, "experts": wl.E, "top_k": wl.K,
+                      "dispatch": "fp8" if wl.fp8 else "bf16"},
+           "us_per_step": round(us_step, 2), "us_per_step_graph": round(graph_us, 2),
+           "GBs": round(total / us_step / 1e3, 1),
+           "kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
+           "kernel_GBs": {"dispatch": round(dis_b / per_kernel["dispatch"] / 1e3, 1),
+                          "combine": round(com_b / per_kernel["combine"] / 1e3, 1)},
+           "kernel_alg_bytes": {"layout": lay_b, "dispatch": dis_b, "combine": com_b}}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-replays", type=int, default=500)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "skew", "hbm", "decode", "tiny"],
+                    help="time another configuration (one short JSON line; the default is the headline)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", nargs="?", const="prefill", default=None,
@@ -393,6 +416,9 @@ def main():
     if args.profile_pass:
         profile_pass(ep, torch, args.profile_pass)
         return 0
+
+    if args.workload != "prefill":
+        return other_workload(ep, torch, args)
 
     s = Setup(ep, torch, "prefill", 0)
     lay_b, dis_b, com_b = s.bytes

@@ -1,0 +1,69 @@
+"""The three calls captured in a HIP graph: every replay, with eager work
+and synchronisation in between, must equal the eager result bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,capacity", [("decode", 0), ("decode", 128), ("prefill", 0)])
+def test_graph_replays_match_eager(gpu, name, capacity):
+    ep = gpu
+    wl = make_workload(name, seed=4)
+    T, H, E, K = wl.T, wl.H, wl.E, wl.K
+    print("case graph", name, capacity, flush=True)
+    dev = "cuda"
+    idx = torch.from_numpy(wl.topk_idx).to(dev)
+    w = torch.from_numpy(wl.topk_weights).to(dev)
+    x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev)
+    R = E * capacity if capacity else T * K
+    y = torch.randn((R, H), device=dev).to(torch.bfloat16)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+    src = torch.empty(R if capacity else T * K, dtype=torch.int32, device=dev)
+    nb = ep.ep_layout_workspace_bytes(T, K, E)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    recv = torch.zeros((R, H), dtype=torch.uint8, device=dev)
+    scale = torch.zeros((R, H // 128), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        if capacity:
+            ep.ep_dispatch_layout_padded(idx, E, capacity, counts, slot, src, ws)
+        else:
+            ep.ep_dispatch_layout(idx, E, counts, offsets, slot, src, ws)
+        ep.ep_dispatch(x, slot, None, ep.EP_RECV_FP8_E4M3_G128, recv, scale, None, num_rows=R)
+        ep.ep_combine(y, slot, w, out, num_rows=R)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (counts, slot, recv, scale, out)]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (counts, slot, out, scale):
+            t.fill_(-1) if t.dtype != torch.bfloat16 else t.zero_()
+        recv.fill_(0x11)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((counts, slot, recv, scale, out), ref):
+            if capacity and a is recv:
+                used = torch.zeros(R, dtype=torch.bool, device=dev)
+                used[slot[slot >= 0].long()] = True
+                assert torch.equal(a[used], b[used]), rep
+            elif capacity and a is scale:
+                continue
+            else:
+                assert torch.equal(a, b), rep

@@ -34,11 +34,15 @@ def assert_bf16_within_one_ulp(got, want):
     assert np.all(np.abs(g - w) <= np.abs(w) * 2.0 ** -7 + 1e-38)
 
 
-@pytest.mark.parametrize("name,seed", [("tiny", 0), ("tiny", 1), ("tiny", 2), ("decode", 0), ("decode", 1),
-                                       ("decode", 2), ("prefill", 0), ("skew", 0), ("skew", 1)])
-def test_fp8_workload_parity(gpu, name, seed):
+@pytest.mark.parametrize("name,seed,over", [("tiny", 0, {}), ("tiny", 1, {}), ("tiny", 2, {}), ("decode", 0, {}),
+                                            ("decode", 1, {}), ("decode", 2, {}), ("prefill", 0, {}),
+                                            ("prefill", 1, {}), ("skew", 0, {}), ("skew", 1, {}),
+                                            ("skew", 2, {"holes_frac": 0.25})])
+def test_fp8_workload_parity(gpu, name, seed, over):
+    """over: config overrides; holes_frac=0.25 gives a quarter of the
+    experts zero popularity (empty experts under skew)."""
     ep = gpu
-    wl = make_workload(name, seed=seed)
+    wl = make_workload(name, seed=seed, **over)
     print("case", name, seed, flush=True)
     slot, off, oslot = check_layout(ep, wl)
     nv = int(off[-1])
