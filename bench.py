@@ -283,11 +283,11 @@ def profile_pass(ep, torch, workload="prefill"):
 
 
 PROFILE_COMMANDS = """\
-cd /tmp && export TMPDIR=/tmp   # then, from the repository root R:
-rocprofv3 --kernel-trace --stats -d R/gpurun_out/prof_trace -o trace --output-format csv -- python3 R/bench.py --profile-pass
-rocprofv3 --pmc FETCH_SIZE -d R/gpurun_out/prof_fetch -o fetch --output-format csv -- python3 R/bench.py --profile-pass
-rocprofv3 --pmc WRITE_SIZE -d R/gpurun_out/prof_write -o write --output-format csv -- python3 R/bench.py --profile-pass
-python3 R/bench.py --summarize-profile R/gpurun_out
+(from the repository root; OUT is any scratch directory; run rocprofv3 with TMPDIR=/tmp)
+rocprofv3 --kernel-trace --stats -d OUT/prof_trace -o trace --output-format csv -- python3 bench.py --profile-pass
+rocprofv3 --pmc FETCH_SIZE -d OUT/prof_fetch -o fetch --output-format csv -- python3 bench.py --profile-pass
+rocprofv3 --pmc WRITE_SIZE -d OUT/prof_write -o write --output-format csv -- python3 bench.py --profile-pass
+python3 bench.py --summarize-profile OUT
 """
 
 COPY_BYTES = 1 << 30  # the profile pass's plain device copy
