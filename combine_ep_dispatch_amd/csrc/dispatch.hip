@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
   const uint32_t t = active ? item / vpt : 0;
   const uint32_t v = item - t * vpt;  // 16-channel vector within the token
   const int32_t* srow = slot + static_cast<size_t>(t) * K;
-  const float* wrow = w + static_cast<size_t>(t) * K;
+  const float* wrow = w != nullptr ? w + static_cast<size_t>(t) * K : nullptr;
   const bool want_w = recv_weight != nullptr && v == 0;
 
   // issue the receive-row loads first; they overlap the token load and the
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
   const uint32_t t = item / vpt;
   const uint32_t v = item - t * vpt;  // 8-channel vector within the token
   const int32_t* srow = slot + static_cast<size_t>(t) * K;
-  const float* wrow = w + static_cast<size_t>(t) * K;
+  const float* wrow = w != nullptr ? w + static_cast<size_t>(t) * K : nullptr;
   const bool want_w = recv_weight != nullptr && v == 0;
   int32_t r[KC];
   float wk[KC];

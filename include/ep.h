@@ -64,8 +64,9 @@ typedef enum {
 /* Human-readable name of a status code (static storage). */
 const char* ep_status_string(int status);
 
-/* Bytes of device workspace ep_dispatch_layout needs for this shape
- * (0 when the single-workgroup path handles it).  Pure host function. */
+/* Bytes of device workspace ep_dispatch_layout and ep_dispatch_layout_padded
+ * need for this shape: 0 up to 65536 entries (T*K), which one launch
+ * handles; beyond, (E+1) int32 per 4096-entry chunk.  Pure host function. */
 size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t top_k, int32_t num_experts);
 
 /*
