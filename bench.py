@@ -348,7 +348,7 @@ def summarize_profile(dirname):
             fb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
             lines.append("%-24s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
                          % (kern, fb, wb, fb + wb, a, (fb + wb) / a))
-            if prefix == "combine_kernel":
+            if prefix == "combine_kernel" and kern.endswith("false>"):  # the weighted combine
                 comb_total = fb + wb
     lines += ["", "combine kernel (the roofline's dominant kernel):",
               "hbm_bytes_per_launch: %.0f" % comb_total,

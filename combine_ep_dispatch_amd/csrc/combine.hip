@@ -60,7 +60,9 @@ __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y,
   }
 }
 
-template <int KT>
+// UNIT: no weights (every weight 1), the backward of dispatch; a separate
+// instantiation so profiles tell the two uses apart.
+template <int KT, bool UNIT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __restrict__ y,
                                                            const int32_t* __restrict__ slot,
                                                            const float* __restrict__ w, uint32_t n_items,
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
   const uint32_t t = item / vpt;
   const uint32_t v = item - t * vpt;  // 8-channel vector within the token
   const int32_t* srow = slot + static_cast<size_t>(t) * K;
-  const float* wrow = w != nullptr ? w + static_cast<size_t>(t) * K : nullptr;
+  const float* wrow = UNIT ? nullptr : w + static_cast<size_t>(t) * K;
 
   float acc[8];
 #pragma unroll
@@ -96,15 +98,18 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w
   const uint32_t n_items = static_cast<uint32_t>(T) * vpt;
   if (n_items == 0) return hipSuccess;
   const dim3 grid((n_items + kThreads - 1) / kThreads), block(kThreads);
-#define EP_COMBINE(KV) \
-  hipLaunchKernelGGL(combine_kernel<KV>, grid, block, 0, stream, y, slot, w, n_items, vpt, H, K, out)
+#define EP_COMBINE(KV)                                                                                 \
+  if (w == nullptr)                                                                                    \
+    hipLaunchKernelGGL((combine_kernel<KV, true>), grid, block, 0, stream, y, slot, w, n_items, vpt, H, K, out); \
+  else                                                                                                 \
+    hipLaunchKernelGGL((combine_kernel<KV, false>), grid, block, 0, stream, y, slot, w, n_items, vpt, H, K, out)
   switch (K) {
-    case 1: EP_COMBINE(1); break;
-    case 2: EP_COMBINE(2); break;
-    case 4: EP_COMBINE(4); break;
-    case 6: EP_COMBINE(6); break;
-    case 8: EP_COMBINE(8); break;
-    default: EP_COMBINE(0); break;
+    case 1: { EP_COMBINE(1); } break;
+    case 2: { EP_COMBINE(2); } break;
+    case 4: { EP_COMBINE(4); } break;
+    case 6: { EP_COMBINE(6); } break;
+    case 8: { EP_COMBINE(8); } break;
+    default: { EP_COMBINE(0); } break;
   }
 #undef EP_COMBINE
   return hipGetLastError();
