@@ -273,7 +273,7 @@ def profile_pass(ep, torch, workload="prefill"):
     s = Setup(ep, torch, workload, 0)
     for _ in range(5):
         s.step()
-    if s.wl.fp8:
+    if workload == "prefill":
         s.backward_buffers(torch)
         for _ in range(3):
             s.dispatch_backward()
@@ -287,6 +287,7 @@ PROFILE_COMMANDS = """\
 rocprofv3 --kernel-trace --stats -d OUT/prof_trace -o trace --output-format csv -- python3 bench.py --profile-pass
 rocprofv3 --pmc FETCH_SIZE -d OUT/prof_fetch -o fetch --output-format csv -- python3 bench.py --profile-pass
 rocprofv3 --pmc WRITE_SIZE -d OUT/prof_write -o write --output-format csv -- python3 bench.py --profile-pass
+rocprofv3 --kernel-trace --stats -d OUT/prof_decode -o decode --output-format csv -- python3 bench.py --profile-pass decode
 python3 bench.py --summarize-profile OUT
 """
 
@@ -321,6 +322,20 @@ def summarize_profile(dirname):
     with open(os.path.join(PROFILES, "prefill_4096x7168_top8_kernel_trace.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
+    dec = rows("prof_decode", "*kernel_trace.csv")
+    if dec:
+        # steady state: the last 3 steps (3 kernels each) of the decode pass
+        fwd = ("layout", "dispatch_fp8_kernel", "combine_kernel<8, false>")
+        ours = [r for r in dec if short(r["Kernel_Name"]).startswith(fwd)][-9:]
+        lines = ["rocprofv3 kernel trace: decode workload (128 tokens, hidden 7168, 256 experts, top-8,",
+                 "FP8 dispatch, BF16 combine), last 3 of 5 eager steps", "", "commands:", PROFILE_COMMANDS,
+                 "%-40s %10s" % ("kernel", "dur_ns")]
+        for r in ours:
+            lines.append("%-40s %10d" % (short(r["Kernel_Name"])[:40],
+                                         int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        with open(os.path.join(PROFILES, "decode_128x7168_top8_kernel_trace.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+
     agg = {}
     for sub, pat in (("prof_fetch", "*counter_collection.csv"), ("prof_write", "*counter_collection.csv")):
         for r in rows(sub, pat):
@@ -339,16 +354,22 @@ def summarize_profile(dirname):
                                       avg[("__amd_rocclr_copyBuffer", "WRITE_SIZE")]),
              "fetch_scale: %.4f" % f_fetch, "write_scale: %.4f" % f_write, ""]
     comb_total = None
-    for prefix, a in (("layout", alg_bytes(T, H, E, K, True)[0]), ("dispatch_fp8_kernel", alg["dispatch_fp8_kernel"]),
-                      ("combine_kernel", alg["combine_kernel"])):
+    d_bwd, _ = backward_bytes(T, H, K)
+    known = (("layout", alg_bytes(T, H, E, K, True)[0]),
+             ("dispatch_fp8_kernel", alg["dispatch_fp8_kernel"]),
+             ("combine_kernel<8, false>", alg["combine_kernel"]),
+             ("combine_kernel<8, true>", d_bwd),  # ep_dispatch_backward
+             ("grad_rows_kernel", 2 * T * H + 8 * T * K + 2 * T * K * H),
+             ("grad_weights_kernel", 2 * T * H + 2 * T * K * H + 8 * T * K))
+    for prefix, a in known:
         for kern in sorted({k for (k, c) in avg if k.startswith(prefix)}):
             fk, wk = avg.get((kern, "FETCH_SIZE")), avg.get((kern, "WRITE_SIZE"))
             if fk is None or wk is None:
                 continue
             fb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
-            lines.append("%-24s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
+            lines.append("%-26s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
                          % (kern, fb, wb, fb + wb, a, (fb + wb) / a))
-            if prefix == "combine_kernel" and kern.endswith("false>"):  # the weighted combine
+            if prefix == "combine_kernel<8, false>":  # the weighted combine
                 comb_total = fb + wb
     lines += ["", "combine kernel (the roofline's dominant kernel):",
               "hbm_bytes_per_launch: %.0f" % comb_total,
@@ -356,8 +377,10 @@ def summarize_profile(dirname):
               "(sha256 prefix of %s; bench.py reports traffic only while it matches)" % ", ".join(COMBINE_SOURCES)]
     with open(TRAFFIC_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
-    for p in ("prefill_4096x7168_top8_kernel_trace.txt", os.path.basename(TRAFFIC_FILE)):
-        print(open(os.path.join(PROFILES, p)).read())
+    for p in ("prefill_4096x7168_top8_kernel_trace.txt", "decode_128x7168_top8_kernel_trace.txt",
+              os.path.basename(TRAFFIC_FILE)):
+        if os.path.exists(os.path.join(PROFILES, p)):
+            print(open(os.path.join(PROFILES, p)).read())
 
 
 def other_workload(ep, torch, args):
