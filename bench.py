@@ -8,14 +8,17 @@ hidden 7168, 256 experts in 8 groups, top-4 groups, top-8 experts).  Inputs
 are seeded synthetic tensors already resident in HBM when timing starts.
 
     python bench.py [--steps K] [--warmup W]        # one JSON line
-    python bench.py --profile-pass                  # short run for rocprofv3
+    python bench.py --workload hbm|skew|decode      # a JSON line for another configuration
+    python bench.py --profile-pass [decode]         # short run for rocprofv3
     python bench.py --summarize-profile DIR         # rocprofv3 csv -> profiles/
 
 The JSON line reports throughput as algorithmic bytes per second (bytes the
 method must move, every one of the K copies counted), the per-kernel
 launch durations measured with HIP events on the launch stream, the
 roofline of the dominant kernel (combine), the decode-size (128 tokens)
-step time, and the oracle's CPU throughput on a bounded sample.
+step time (eager launches and as a replayed HIP graph, packed and with the
+low-latency padded layout), the backward helpers at the prefill size, and
+the oracle's CPU throughput on the same workload.
 """
 
 import argparse
