@@ -501,6 +501,13 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic},
     }
+    if traffic is not None:
+        # the same launch duration over the bytes the HBM counters saw
+        rec["roofline"]["traffic_GBs"] = round(traffic / (comb_us * 1e-6) / 1e9, 1)
+    rec["context_pages"] = {
+        "note": "DeepEP on H800, multi-GPU all-to-all over interconnects; context, not a target",
+        "normal_kernels_nvlink_GBs": "153-158", "normal_kernels_rdma_GBs": "43-47",
+        "low_latency_us": 163, "low_latency_rdma_GBs": "39-46"}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(s.wl, args.cpu_budget)
     print(json.dumps(rec), flush=True)
