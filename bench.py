@@ -16,8 +16,9 @@ The JSON line reports throughput as algorithmic bytes per second (bytes the
 method must move, every one of the K copies counted), the per-kernel
 launch durations measured with HIP events on the launch stream, the
 roofline of the dominant kernel (combine), the decode-size (128 tokens)
-step time (eager launches and as a replayed HIP graph, packed and with the
-low-latency padded layout), the backward helpers at the prefill size, and
+step time (eager launches through the checked binding and through
+StepPlan, and as a replayed HIP graph, packed and with the low-latency
+padded layout), the backward helpers at the prefill size, and
 the oracle's CPU throughput on the same workload.
 """
 
@@ -460,7 +461,10 @@ def main():
     d = Setup(ep, torch, "decode", 0)
     d_us, d_per, _ = time_steps(torch, d, 200, 10)
     d_graph = time_graph(torch, d, args.decode_replays)
-    del d
+    # the same step through StepPlan: buffers checked once, three bare C calls
+    dp = ep.StepPlan(d.idx, d.w, d.x, d.wl.E, y=d.y)
+    dp_us, _, _ = time_steps(torch, dp, 200, 10)
+    del d, dp
     # low-latency form: 128 rows per expert ([E, 128, H] receive buffer)
     dl = Setup(ep, torch, "decode", 0, capacity=128)
     dl_us, dl_per, _ = time_steps(torch, dl, 200, 10)
@@ -490,7 +494,8 @@ def main():
         "us_per_step_graph": round(graph_us, 2),
         "kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "kernel_alg_bytes": {"layout": lay_b, "dispatch": dis_b, "combine": com_b},
-        "decode_128tok_us": {"stream": round(d_us, 2), "graph": round(d_graph, 2),
+        "decode_128tok_us": {"stream": round(d_us, 2), "stream_step_plan": round(dp_us, 2),
+                             "graph": round(d_graph, 2),
                              "kernel_us": {k: round(v, 2) for k, v in d_per.items()},
                              "low_latency_padded_128": {"stream": round(dl_us, 2), "graph": round(dl_graph, 2),
                                                         "kernel_us": {k: round(v, 2) for k, v in dl_per.items()}}},

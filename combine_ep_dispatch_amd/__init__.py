@@ -39,3 +39,4 @@ from .api import (  # noqa: F401
     low_latency_combine,
     low_latency_dispatch,
 )
+from .plan import StepPlan  # noqa: F401

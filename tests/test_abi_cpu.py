@@ -125,3 +125,14 @@ def test_padded_layout_rejects_bad_arguments(lib):
     assert call(s=None) == lib.EP_ERR_INVALID_ARG
     assert call(E=2000) == lib.EP_ERR_UNSUPPORTED
     assert call(T=8200, K=8, E=256) == lib.EP_ERR_INVALID_ARG  # needs a workspace
+
+
+def test_step_plan_rejects_host_tensors():
+    """StepPlan validates its buffers before any C call (no GPU needed)."""
+    import torch
+    ep = pytest.importorskip("combine_ep_dispatch_amd")
+    idx = torch.zeros((4, 2), dtype=torch.int32)
+    w = torch.ones((4, 2), dtype=torch.float32)
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU device"):
+        ep.StepPlan(idx, w, x, 8)
