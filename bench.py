@@ -127,6 +127,16 @@ class Setup:
         self.dispatch()
         self.combine()
 
+    def layout_dispatch(self):
+        # one call for layout + dispatch (one launch up to 3072 entries)
+        self.ep.ep_layout_dispatch(self.idx, self.x, None, self.wl.E, self.capacity, self.fmt, self.counts,
+                                   None if self.capacity else self.offsets, self.slot, self.src, self.recv,
+                                   self.scale, None, self.ws)
+
+    def step_fused(self):
+        self.layout_dispatch()
+        self.combine()
+
     def backward_buffers(self, torch):
         T, H, K = self.wl.T, self.wl.H, self.wl.K
         self.grad_out = torch.randn((T, H), device="cuda").to(torch.bfloat16)
@@ -179,13 +189,29 @@ def time_steps(torch, s, steps, warmup):
     return us_step, {k: sum(v) / len(v) for k, v in per.items()}, wall
 
 
-def time_graph(torch, s, replays):
-    """Step captured once in a HIP graph and replayed; returns µs per step."""
-    s.step()
+def time_loop(torch, fn, steps, warmup):
+    """Mean µs of fn over `steps` back-to-back calls, HIP events only at the
+    ends (on the launch stream)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / steps
+
+
+def time_graph(torch, step, replays):
+    """`step` captured once in a HIP graph and replayed; returns µs per step."""
+    step()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        s.step()
+        step()
     for _ in range(5):
         g.replay()
     torch.cuda.synchronize()
@@ -277,6 +303,9 @@ def profile_pass(ep, torch, workload="prefill"):
     s = Setup(ep, torch, workload, 0)
     for _ in range(5):
         s.step()
+    if workload == "decode":
+        for _ in range(5):
+            s.step_fused()
     if workload == "prefill":
         s.backward_buffers(torch)
         for _ in range(3):
@@ -328,13 +357,20 @@ def summarize_profile(dirname):
 
     dec = rows("prof_decode", "*kernel_trace.csv")
     if dec:
-        # steady state: the last 3 steps (3 kernels each) of the decode pass
+        # steady state: the last 3 of 5 three-call steps (layout, dispatch,
+        # combine), then the last 3 of 5 fused steps (layout_dispatch, combine)
         fwd = ("layout", "dispatch_fp8_kernel", "combine_kernel<8, false>")
-        ours = [r for r in dec if short(r["Kernel_Name"]).startswith(fwd)][-9:]
+        ours = [r for r in dec if short(r["Kernel_Name"]).startswith(fwd)]
+        three = ours[:15][-9:]
+        fused = ours[15:][-6:]
         lines = ["rocprofv3 kernel trace: decode workload (128 tokens, hidden 7168, 256 experts, top-8,",
-                 "FP8 dispatch, BF16 combine), last 3 of 5 eager steps", "", "commands:", PROFILE_COMMANDS,
+                 "FP8 dispatch, BF16 combine): last 3 of 5 eager three-call steps, then last 3 of 5 eager",
+                 "fused steps (layout and dispatch in one launch)", "", "commands:", PROFILE_COMMANDS,
                  "%-40s %10s" % ("kernel", "dur_ns")]
-        for r in ours:
+        for r in three + [None] + fused:
+            if r is None:
+                lines.append("")
+                continue
             lines.append("%-40s %10d" % (short(r["Kernel_Name"])[:40],
                                          int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
         with open(os.path.join(PROFILES, "decode_128x7168_top8_kernel_trace.txt"), "w") as f:
@@ -392,7 +428,7 @@ def other_workload(ep, torch, args):
     s = Setup(ep, torch, args.workload, 0)
     lay_b, dis_b, com_b = s.bytes
     us_step, per_kernel, _ = time_steps(torch, s, args.steps, args.warmup)
-    graph_us = time_graph(torch, s, 20 if s.wl.T > 8192 else 200)
+    graph_us = time_graph(torch, s.step, 20 if s.wl.T > 8192 else 200)
     total = lay_b + dis_b + com_b
     wl = s.wl
     rec = {"metric": "step µs and algorithmic GB/s", "workload": args.workload,
@@ -452,24 +488,29 @@ def main():
     us_step, per_kernel, wall = time_steps(torch, s, args.steps, args.warmup)
     total_b = lay_b + dis_b + com_b
     gbs = total_b / (us_step * 1e-6) / 1e9
-    graph_us = time_graph(torch, s, 50)
+    graph_us = time_graph(torch, s.step, 50)
     s.backward_buffers(torch)
     db_b, cb_b = backward_bytes(s.wl.T, s.wl.H, s.wl.K)
     db_us = time_calls(torch, s.dispatch_backward, 30)
     cb_us = time_calls(torch, s.combine_backward, 30)
 
-    d = Setup(ep, torch, "decode", 0)
-    d_us, d_per, _ = time_steps(torch, d, 200, 10)
-    d_graph = time_graph(torch, d, args.decode_replays)
-    # the same step through StepPlan: buffers checked once, three bare C calls
-    dp = ep.StepPlan(d.idx, d.w, d.x, d.wl.E, y=d.y)
-    dp_us, _, _ = time_steps(torch, dp, 200, 10)
-    del d, dp
-    # low-latency form: 128 rows per expert ([E, 128, H] receive buffer)
-    dl = Setup(ep, torch, "decode", 0, capacity=128)
-    dl_us, dl_per, _ = time_steps(torch, dl, 200, 10)
-    dl_graph = time_graph(torch, dl, args.decode_replays)
-    del dl
+    # decode: three calls (layout, dispatch, combine), then the fused form
+    # (layout + dispatch in one launch, then combine), each eager through
+    # the checked binding, eager through StepPlan (buffers checked once) and
+    # as a replayed HIP graph; packed and low-latency padded layouts
+    decode = {}
+    for cap in (0, 128):
+        d = Setup(ep, torch, "decode", 0, capacity=cap)
+        d_us, d_per, _ = time_steps(torch, d, 200, 10)
+        rec_d = {"stream": round(d_us, 2), "graph": round(time_graph(torch, d.step, args.decode_replays), 2),
+                 "kernel_us": {k: round(v, 2) for k, v in d_per.items()}}
+        plan = ep.StepPlan(d.idx, d.w, d.x, d.wl.E, capacity=cap, y=d.y)
+        rec_d["fused"] = {"stream": round(time_loop(torch, d.step_fused, 200, 10), 2),
+                          "stream_step_plan": round(time_loop(torch, plan.step, 200, 10), 2),
+                          "graph": round(time_graph(torch, d.step_fused, args.decode_replays), 2),
+                          "kernel_us": {"layout_dispatch": round(time_calls(torch, d.layout_dispatch, 200), 2)}}
+        decode[cap] = rec_d
+        del d, plan
 
     comb_us = per_kernel["combine"]
     achieved = com_b / (comb_us * 1e-6) / 1e9
@@ -494,11 +535,7 @@ def main():
         "us_per_step_graph": round(graph_us, 2),
         "kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "kernel_alg_bytes": {"layout": lay_b, "dispatch": dis_b, "combine": com_b},
-        "decode_128tok_us": {"stream": round(d_us, 2), "stream_step_plan": round(dp_us, 2),
-                             "graph": round(d_graph, 2),
-                             "kernel_us": {k: round(v, 2) for k, v in d_per.items()},
-                             "low_latency_padded_128": {"stream": round(dl_us, 2), "graph": round(dl_graph, 2),
-                                                        "kernel_us": {k: round(v, 2) for k, v in dl_per.items()}}},
+        "decode_128tok_us": dict(decode[0], low_latency_padded_128=decode[128]),
         "backward_us": {"dispatch_backward": round(db_us, 2), "combine_backward": round(cb_us, 2),
                         "dispatch_backward_GBs": round(db_b / db_us / 1e3, 1),
                         "combine_backward_GBs": round(cb_b / cb_us / 1e3, 1)},

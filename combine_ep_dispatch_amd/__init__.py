@@ -33,6 +33,7 @@ from .api import (  # noqa: F401
     ep_dispatch,
     ep_dispatch_layout,
     ep_dispatch_layout_padded,
+    ep_layout_dispatch,
     ep_layout_workspace_bytes,
     layout,
     layout_padded,

@@ -26,6 +26,7 @@ EXPORTS = (
     "ep_dispatch_layout",
     "ep_dispatch_layout_padded",
     "ep_dispatch",
+    "ep_layout_dispatch",
     "ep_combine",
     "ep_dispatch_backward",
     "ep_combine_backward",
@@ -60,6 +61,8 @@ def _load():
     lib.ep_dispatch_layout_padded.restype = ctypes.c_int
     lib.ep_dispatch.argtypes = [p, i64, i32, i32, p, p, i32, p, p, p, p]
     lib.ep_dispatch.restype = ctypes.c_int
+    lib.ep_layout_dispatch.argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p, p, p, p, sz, p]
+    lib.ep_layout_dispatch.restype = ctypes.c_int
     lib.ep_combine.argtypes = [p, p, p, i64, i32, i32, p, p]
     lib.ep_combine.restype = ctypes.c_int
     lib.ep_dispatch_backward.argtypes = [p, p, i64, i32, i32, p, p]

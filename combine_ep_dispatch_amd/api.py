@@ -125,6 +125,57 @@ def ep_dispatch(x, slot, topk_weights, format, recv_x, recv_scale=None, recv_wei
         recv_weight.data_ptr() if recv_weight is not None else None, _stream(stream)))
 
 
+def ep_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format, tokens_per_expert,
+                       expert_offset, slot, src_token, recv_x, recv_scale=None, recv_weight=None, workspace=None,
+                       stream=None):
+    """Layout and dispatch in one call (one launch up to 3072 entries).
+    capacity 0: packed layout (expert_offset [E+1], src_token [T*K], T*K
+    receive rows); capacity > 0: padded layout (expert_offset None,
+    src_token [E*capacity], E*capacity receive rows)."""
+    _need(topk_idx, "topk_idx", _I32)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T, K]")
+    T, K = topk_idx.shape
+    E, cap = int(num_experts), int(capacity)
+    if cap < 0:
+        raise ValueError("capacity must be >= 0")
+    R = E * cap if cap else T * K
+    _need(x, "x", _BF16)
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H]")
+    H = x.shape[1]
+    _need(tokens_per_expert, "tokens_per_expert", _I32, (E,))
+    if cap == 0:
+        _need(expert_offset, "expert_offset", _I32, (E + 1,))
+    elif expert_offset is not None:
+        raise ValueError("expert_offset is not used by the padded layout; pass None")
+    _need(slot, "slot", _I32, (T, K))
+    _need(src_token, "src_token", _I32, (R,))
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", _F32, (T, K))
+    if format == EP_RECV_FP8_E4M3_G128:
+        if H % 128:
+            raise ValueError("FP8 dispatch needs hidden % 128 == 0")
+        _need(recv_x, "recv_x", _U8, (R, H))
+        _need(recv_scale, "recv_scale", _F32, (R, H // 128))
+    elif format == EP_RECV_BF16:
+        _need(recv_x, "recv_x", _BF16, (R, H))
+    else:
+        raise ValueError("unknown receive format %r" % (format,))
+    if recv_weight is not None:
+        _need(recv_weight, "recv_weight", _F32, (R,))
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8, torch.int32))
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check("ep_layout_dispatch", LIB.ep_layout_dispatch(
+        topk_idx.data_ptr(), x.data_ptr(), topk_weights.data_ptr() if topk_weights is not None else None, T, H, K,
+        E, cap, int(format), tokens_per_expert.data_ptr(),
+        expert_offset.data_ptr() if expert_offset is not None else None, slot.data_ptr(), src_token.data_ptr(),
+        recv_x.data_ptr(), recv_scale.data_ptr() if recv_scale is not None else None,
+        recv_weight.data_ptr() if recv_weight is not None else None, ws_ptr, ws_bytes, _stream(stream)))
+
+
 def ep_combine(y, slot, topk_weights, out, stream=None, num_rows=None):
     """num_rows: rows of y (T*K by default; E*capacity for a padded slot)."""
     _need(slot, "slot", _I32)
@@ -218,25 +269,39 @@ def dispatch(x, topk_idx, topk_weights, num_experts, fp8=True, handle=None, stre
     ``topk_weights`` is None).  Rows expert_offset[e] .. expert_offset[e+1]-1
     belong to expert e.
     """
-    if handle is None:
-        handle = layout(topk_idx, num_experts, stream)
     T, H = x.shape
-    K = handle.slot.shape[1]
     dev = x.device
+    if handle is None:
+        if topk_idx.dtype != torch.int32:
+            topk_idx = topk_idx.to(torch.int32)
+        topk_idx = topk_idx.contiguous()
+    K = handle.slot.shape[1] if handle is not None else topk_idx.shape[1]
     recv_weight = None
     if topk_weights is not None:
         topk_weights = topk_weights.to(torch.float32).contiguous()
         recv_weight = torch.empty(T * K, dtype=torch.float32, device=dev)
+    fmt = EP_RECV_FP8_E4M3_G128 if fp8 else EP_RECV_BF16
     if fp8:
         recv_x = torch.empty((T * K, H), dtype=torch.uint8, device=dev)
         recv_scale = torch.empty((T * K, H // 128), dtype=torch.float32, device=dev)
-        ep_dispatch(x, handle.slot, topk_weights, EP_RECV_FP8_E4M3_G128, recv_x, recv_scale, recv_weight,
-                    stream)
     else:
         recv_x = torch.empty((T * K, H), dtype=torch.bfloat16, device=dev)
         recv_scale = None
-        ep_dispatch(x, handle.slot, topk_weights, EP_RECV_BF16, recv_x, None, recv_weight, stream)
-    return recv_x, recv_scale, recv_weight, handle
+    if handle is not None:
+        ep_dispatch(x, handle.slot, topk_weights, fmt, recv_x, recv_scale, recv_weight, stream)
+        return recv_x, recv_scale, recv_weight, handle
+    E = int(num_experts)
+    if not 1 <= E <= EP_MAX_EXPERTS or not 1 <= K <= EP_MAX_TOPK:
+        raise ValueError("unsupported num_experts=%d / top_k=%d" % (E, K))
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+    src = torch.empty(T * K, dtype=torch.int32, device=dev)
+    nb = ep_layout_workspace_bytes(T, K, E)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    ep_layout_dispatch(topk_idx, x, topk_weights, E, 0, fmt, counts, offsets, slot, src, recv_x, recv_scale,
+                       recv_weight, ws, stream)
+    return recv_x, recv_scale, recv_weight, Handle(counts, offsets, slot, src, E)
 
 
 def combine(y, handle, topk_weights, stream=None):
@@ -273,20 +338,31 @@ def low_latency_dispatch(x, topk_idx, num_max_tokens, num_experts, fp8=True, str
     Returns (recv_x [E, num_max_tokens, H], recv_scale [E, num_max_tokens,
     H/128] or None, recv_expert_count [E], handle).
     """
-    h = layout_padded(topk_idx, num_experts, num_max_tokens, stream)
+    if topk_idx.dtype != torch.int32:
+        topk_idx = topk_idx.to(torch.int32)
+    topk_idx = topk_idx.contiguous()
     T, H = x.shape
-    E, cap = h.num_experts, h.capacity
+    K = topk_idx.shape[1]
+    E, cap = int(num_experts), int(num_max_tokens)
+    if cap < 1:
+        raise ValueError("num_max_tokens must be >= 1")
     dev = x.device
+    count = torch.empty(E, dtype=torch.int32, device=dev)
+    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+    src = torch.empty(E * cap, dtype=torch.int32, device=dev)
+    nb = ep_layout_workspace_bytes(T, K, E)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
     if fp8:
         recv_x = torch.empty((E * cap, H), dtype=torch.uint8, device=dev)
         recv_scale = torch.empty((E * cap, H // 128), dtype=torch.float32, device=dev)
-        ep_dispatch(x, h.slot, None, EP_RECV_FP8_E4M3_G128, recv_x, recv_scale, None, stream, num_rows=E * cap)
-        recv_scale = recv_scale.view(E, cap, H // 128)
     else:
         recv_x = torch.empty((E * cap, H), dtype=torch.bfloat16, device=dev)
         recv_scale = None
-        ep_dispatch(x, h.slot, None, EP_RECV_BF16, recv_x, None, None, stream, num_rows=E * cap)
-    return recv_x.view(E, cap, H), recv_scale, h.recv_expert_count, h
+    ep_layout_dispatch(topk_idx, x, None, E, cap, EP_RECV_FP8_E4M3_G128 if fp8 else EP_RECV_BF16, count, None,
+                       slot, src, recv_x, recv_scale, None, ws, stream)
+    if recv_scale is not None:
+        recv_scale = recv_scale.view(E, cap, H // 128)
+    return recv_x.view(E, cap, H), recv_scale, count, PaddedHandle(count, slot, src, E, cap)
 
 
 def low_latency_combine(y, handle, topk_weights, stream=None):

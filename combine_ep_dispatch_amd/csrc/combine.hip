@@ -27,8 +27,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 // Adds the terms of k = k0 .. k0+KC-1 (those < K) to acc, in ascending k.
 template <int KC>
 __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y, const int32_t* __restrict__ srow,

@@ -38,8 +38,6 @@ constexpr int kRowThreads = 256;
 constexpr int kMaxWaves = 16;  // workgroups of up to 1024 lanes
 constexpr int kMaxK = 32;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));

@@ -29,8 +29,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 // Receive rows (and weights) of entries k0 .. k0+KC-1 of one token, loaded
 // together before any store so their latencies overlap.
 template <int KC>
@@ -71,27 +69,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     a = __builtin_nontemporal_load(src);
     b = __builtin_nontemporal_load(src + 1);
   }
-  float f[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf16_lo(a[i]);
-    f[2 * i + 1] = bf16_hi(a[i]);
-    f[8 + 2 * i] = bf16_lo(b[i]);
-    f[8 + 2 * i + 1] = bf16_hi(b[i]);
-  }
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(f[i]) & 0x7FFFFFFFu);
-  m = max8_u32(m);  // all 8 lanes of the group now hold its |max| bits
-
-  float s = __uint_as_float(m) / 448.0f;
-  s = s < 0x1p-126f ? 0x1p-126f : s;
-  s = m == 0 ? 1.0f : s;
-
-  u32x4 q;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    q[j] = f32x4_to_e4m3(f[4 * j] / s, f[4 * j + 1] / s, f[4 * j + 2] / s, f[4 * j + 3] / s);
+  float s;
+  const u32x4 q = quantize16_e4m3(a, b, s);
 
   if (!active) return;
   const uint32_t G = static_cast<uint32_t>(H) / kGroup;

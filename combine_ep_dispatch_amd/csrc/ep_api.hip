@@ -27,6 +27,54 @@ ep_status check_common(int64_t T, int32_t K) {
   return EP_OK;
 }
 
+// Checks of the layout arguments (capacity 0: packed layout with offsets;
+// capacity > 0: padded layout, offsets unused).
+ep_status check_layout(const int32_t* topk_idx, int64_t T, int32_t K, int32_t E, int32_t capacity,
+                       const int32_t* counts, const int32_t* offsets, const int32_t* slot, const int32_t* src,
+                       const void* workspace, size_t workspace_bytes) {
+  ep_status st = check_common(T, K);
+  if (st != EP_OK) return st;
+  if (E < 1 || capacity < 0) return EP_ERR_INVALID_ARG;
+  if (E > EP_MAX_EXPERTS) return EP_ERR_UNSUPPORTED;
+  if (!counts || !aligned(counts, 4)) return EP_ERR_INVALID_ARG;
+  if (capacity == 0) {
+    if (!offsets || !aligned(offsets, 4)) return EP_ERR_INVALID_ARG;
+  } else {
+    if (static_cast<int64_t>(E) * capacity >= (int64_t(1) << 31)) return EP_ERR_INVALID_ARG;
+    if (!src || !aligned(src, 4)) return EP_ERR_INVALID_ARG;
+  }
+  const int64_t rows = T * K;
+  if (rows > 0) {
+    if (!topk_idx || !slot || !src) return EP_ERR_INVALID_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(slot, 4) || !aligned(src, 4)) return EP_ERR_INVALID_ARG;
+  }
+  const size_t need = ep::layout_workspace_bytes(rows, E);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return EP_ERR_INVALID_ARG;
+  return EP_OK;
+}
+
+// Checks of the dispatch arguments other than slot; the buffers are only
+// checked when there are tokens.
+ep_status check_dispatch(const void* x, int64_t T, int32_t H, int32_t K, const float* topk_weights, int32_t format,
+                         const void* recv_x, const float* recv_scale, const float* recv_weight) {
+  ep_status st = check_common(T, K);
+  if (st != EP_OK) return st;
+  if (H <= 0) return EP_ERR_INVALID_ARG;
+  if (format != EP_RECV_FP8_E4M3_G128 && format != EP_RECV_BF16) return EP_ERR_INVALID_ARG;
+  if (format == EP_RECV_FP8_E4M3_G128 && H % 128 != 0) return EP_ERR_INVALID_ARG;
+  if (H % 8 != 0) return EP_ERR_INVALID_ARG;
+  if (recv_weight != nullptr && topk_weights == nullptr) return EP_ERR_INVALID_ARG;
+  if (T * H >= (int64_t(1) << 35)) return EP_ERR_UNSUPPORTED;
+  if (T == 0) return EP_OK;
+  if (!x || !recv_x) return EP_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(recv_x, 16)) return EP_ERR_INVALID_ARG;
+  if (topk_weights && !aligned(topk_weights, 4)) return EP_ERR_INVALID_ARG;
+  if (recv_weight && !aligned(recv_weight, 4)) return EP_ERR_INVALID_ARG;
+  if (format == EP_RECV_FP8_E4M3_G128 && (!recv_scale || !aligned(recv_scale, 4))) return EP_ERR_INVALID_ARG;
+  return EP_OK;
+}
+
 }  // namespace
 
 EP_API const char* ep_status_string(int status) {
@@ -48,21 +96,10 @@ EP_API ep_status ep_dispatch_layout(const int32_t* topk_idx, int64_t num_tokens,
                                     int32_t num_experts, int32_t* tokens_per_expert, int32_t* expert_offset,
                                     int32_t* slot, int32_t* src_token, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-  ep_status st = check_common(num_tokens, top_k);
+  ep_status st = check_layout(topk_idx, num_tokens, top_k, num_experts, 0, tokens_per_expert, expert_offset, slot,
+                              src_token, workspace, workspace_bytes);
   if (st != EP_OK) return st;
-  if (num_experts < 1) return EP_ERR_INVALID_ARG;
-  if (num_experts > EP_MAX_EXPERTS) return EP_ERR_UNSUPPORTED;
-  if (!tokens_per_expert || !expert_offset) return EP_ERR_INVALID_ARG;
-  if (!aligned(tokens_per_expert, 4) || !aligned(expert_offset, 4)) return EP_ERR_INVALID_ARG;
-  const int64_t rows = num_tokens * top_k;
-  if (rows > 0) {
-    if (!topk_idx || !slot || !src_token) return EP_ERR_INVALID_ARG;
-    if (!aligned(topk_idx, 4) || !aligned(slot, 4) || !aligned(src_token, 4)) return EP_ERR_INVALID_ARG;
-  }
-  const size_t need = ep::layout_workspace_bytes(rows, num_experts);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
-    return EP_ERR_INVALID_ARG;
-  return from_hip(ep::launch_layout(topk_idx, static_cast<int32_t>(rows), top_k, num_experts, 0,
+  return from_hip(ep::launch_layout(topk_idx, static_cast<int32_t>(num_tokens * top_k), top_k, num_experts, 0,
                                     tokens_per_expert, expert_offset, slot, src_token, workspace,
                                     static_cast<hipStream_t>(stream)));
 }
@@ -73,50 +110,49 @@ EP_API ep_status ep_dispatch_layout_padded(const int32_t* topk_idx, int64_t num_
                                            size_t workspace_bytes, void* stream) {
   ep_status st = check_common(num_tokens, top_k);
   if (st != EP_OK) return st;
-  if (num_experts < 1 || capacity < 1) return EP_ERR_INVALID_ARG;
-  if (num_experts > EP_MAX_EXPERTS) return EP_ERR_UNSUPPORTED;
-  if (static_cast<int64_t>(num_experts) * capacity >= (int64_t(1) << 31)) return EP_ERR_INVALID_ARG;
-  if (!recv_expert_count || !src_token) return EP_ERR_INVALID_ARG;
-  if (!aligned(recv_expert_count, 4) || !aligned(src_token, 4)) return EP_ERR_INVALID_ARG;
-  const int64_t rows = num_tokens * top_k;
-  if (rows > 0) {
-    if (!topk_idx || !slot) return EP_ERR_INVALID_ARG;
-    if (!aligned(topk_idx, 4) || !aligned(slot, 4)) return EP_ERR_INVALID_ARG;
-  }
-  const size_t need = ep::layout_workspace_bytes(rows, num_experts);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
-    return EP_ERR_INVALID_ARG;
-  return from_hip(ep::launch_layout(topk_idx, static_cast<int32_t>(rows), top_k, num_experts, capacity,
-                                    recv_expert_count, nullptr, slot, src_token, workspace,
+  if (capacity < 1) return EP_ERR_INVALID_ARG;
+  st = check_layout(topk_idx, num_tokens, top_k, num_experts, capacity, recv_expert_count, nullptr, slot,
+                    src_token, workspace, workspace_bytes);
+  if (st != EP_OK) return st;
+  return from_hip(ep::launch_layout(topk_idx, static_cast<int32_t>(num_tokens * top_k), top_k, num_experts,
+                                    capacity, recv_expert_count, nullptr, slot, src_token, workspace,
                                     static_cast<hipStream_t>(stream)));
 }
 
 EP_API ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, int32_t top_k,
                              const int32_t* slot, const float* topk_weights, int32_t format, void* recv_x,
                              float* recv_scale, float* recv_weight, void* stream) {
-  ep_status st = check_common(num_tokens, top_k);
+  ep_status st = check_dispatch(x, num_tokens, hidden, top_k, topk_weights, format, recv_x, recv_scale, recv_weight);
   if (st != EP_OK) return st;
-  if (hidden <= 0) return EP_ERR_INVALID_ARG;
-  if (format != EP_RECV_FP8_E4M3_G128 && format != EP_RECV_BF16) return EP_ERR_INVALID_ARG;
-  if (format == EP_RECV_FP8_E4M3_G128 && hidden % 128 != 0) return EP_ERR_INVALID_ARG;
-  if (hidden % 8 != 0) return EP_ERR_INVALID_ARG;
-  if (recv_weight != nullptr && topk_weights == nullptr) return EP_ERR_INVALID_ARG;
-  if (num_tokens * hidden >= (int64_t(1) << 35)) return EP_ERR_UNSUPPORTED;
   if (num_tokens == 0) return EP_OK;
-  if (!x || !slot || !recv_x) return EP_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(slot, 4)) return EP_ERR_INVALID_ARG;
-  if (topk_weights && !aligned(topk_weights, 4)) return EP_ERR_INVALID_ARG;
-  if (recv_weight && !aligned(recv_weight, 4)) return EP_ERR_INVALID_ARG;
+  if (!slot || !aligned(slot, 4)) return EP_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t T = static_cast<int32_t>(num_tokens);
-  if (format == EP_RECV_FP8_E4M3_G128) {
-    if (!recv_scale || !aligned(recv_scale, 4)) return EP_ERR_INVALID_ARG;
+  if (format == EP_RECV_FP8_E4M3_G128)
     return from_hip(ep::launch_dispatch_fp8(static_cast<const uint16_t*>(x), T, hidden, top_k, slot,
                                             topk_weights, static_cast<uint8_t*>(recv_x), recv_scale,
                                             recv_weight, s));
-  }
   return from_hip(ep::launch_dispatch_bf16(static_cast<const uint16_t*>(x), T, hidden, top_k, slot,
                                            topk_weights, static_cast<uint16_t*>(recv_x), recv_weight, s));
+}
+
+EP_API ep_status ep_layout_dispatch(const int32_t* topk_idx, const void* x, const float* topk_weights,
+                                    int64_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
+                                    int32_t capacity, int32_t format, int32_t* tokens_per_expert,
+                                    int32_t* expert_offset, int32_t* slot, int32_t* src_token, void* recv_x,
+                                    float* recv_scale, float* recv_weight, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  ep_status st = check_layout(topk_idx, num_tokens, top_k, num_experts, capacity, tokens_per_expert,
+                              capacity == 0 ? expert_offset : nullptr, slot, src_token, workspace,
+                              workspace_bytes);
+  if (st != EP_OK) return st;
+  st = check_dispatch(x, num_tokens, hidden, top_k, topk_weights, format, recv_x, recv_scale, recv_weight);
+  if (st != EP_OK) return st;
+  return from_hip(ep::launch_layout_dispatch(
+      topk_idx, static_cast<const uint16_t*>(x), topk_weights, static_cast<int32_t>(num_tokens), hidden, top_k,
+      num_experts, capacity, format == EP_RECV_FP8_E4M3_G128, tokens_per_expert,
+      capacity == 0 ? expert_offset : nullptr, slot, src_token, recv_x, recv_scale, recv_weight, workspace,
+      static_cast<hipStream_t>(stream)));
 }
 
 EP_API ep_status ep_combine(const void* y, const int32_t* slot, const float* topk_weights, int64_t num_tokens,

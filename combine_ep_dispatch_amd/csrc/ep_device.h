@@ -10,6 +10,8 @@ namespace ep {
 constexpr int kWave = 64;
 constexpr int kGroup = 128;  // channels per FP8 scale group
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // ---- wavefront primitives -------------------------------------------------
 
 __device__ __forceinline__ uint64_t wave_ballot(bool p) {
@@ -31,6 +33,44 @@ __device__ __forceinline__ uint32_t max8_u32(uint32_t v) {
   v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
   v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false)));
   return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum of data[0..n) in LDS, in place.  Every thread of the
+// block must call it.  wave_tot needs blockDim.x / 64 ints of LDS.
+__device__ inline void block_exclusive_scan(int* data, int n, int* wave_tot) {
+  const int tid = threadIdx.x, bs = blockDim.x;
+  const int lane = tid & (kWave - 1), w = tid / kWave, nw = bs / kWave;
+  const int per = (n + bs - 1) / bs;
+  const int beg = min(n, tid * per), end = min(n, beg + per);
+  int local = 0;
+  for (int i = beg; i < end; ++i) local += data[i];
+  const int incl = wave_inclusive_scan(local);
+  if (lane == kWave - 1) wave_tot[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    const int v = lane < nw ? wave_tot[lane] : 0;
+    const int s = wave_inclusive_scan(v);
+    if (lane < nw) wave_tot[lane] = s - v;
+  }
+  __syncthreads();
+  int run = wave_tot[w] + incl - local;
+  for (int i = beg; i < end; ++i) {
+    const int c = data[i];
+    data[i] = run;
+    run += c;
+  }
+  __syncthreads();
 }
 
 // ---- number formats -------------------------------------------------------
@@ -58,6 +98,37 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, flo
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return static_cast<uint32_t>(w);
+}
+
+// One lane's 16 consecutive channels (two 16-byte vectors of BF16 bits) ->
+// 16 E4M3 codes, and the binary32 scale of their 128-channel group, which
+// the 8 aligned lanes 8j..8j+7 hold together (all 8 must call this).
+// Scale rule: s = RN32(amax / 448) with a correctly rounded division, 1 for
+// an all-zero group, floored at 2^-126; code = E4M3_RNE(RN32(x / s)).
+__device__ __forceinline__ u32x4 quantize16_e4m3(u32x4 a, u32x4 b, float& scale) {
+  float f[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(a[i]);
+    f[2 * i + 1] = bf16_hi(a[i]);
+    f[8 + 2 * i] = bf16_lo(b[i]);
+    f[8 + 2 * i + 1] = bf16_hi(b[i]);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+  m = max8_u32(m);  // all 8 lanes of the group now hold its |max| bits
+
+  float s = __uint_as_float(m) / 448.0f;
+  s = s < 0x1p-126f ? 0x1p-126f : s;
+  s = m == 0 ? 1.0f : s;
+
+  u32x4 q;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    q[j] = f32x4_to_e4m3(f[4 * j] / s, f[4 * j + 1] / s, f[4 * j + 2] / s, f[4 * j + 3] / s);
+  scale = s;
+  return q;
 }
 
 }  // namespace ep

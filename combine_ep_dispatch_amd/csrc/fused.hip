@@ -1,0 +1,315 @@
+// Layout and dispatch in one launch, for small batches (decode).
+//
+// The pages' dispatch call takes the tokens with their routing and returns
+// the received rows together with the handle ([P4 "使用示例 › MoE 训练中的
+// 应用"]); its low-latency form fills per-expert buffers of a fixed number
+// of rows and reports per-expert counts ([P4 "使用示例 › 推理解码阶段的应用"]).
+// At decode sizes a launch costs a few microseconds of mostly fixed latency,
+// so this kernel writes everything the layout kernels and the dispatch
+// kernel would, bit for bit, in a single launch.
+//
+// A token's receive rows have a closed form as counts over all n = T*K
+// entries.  With key = expert for a valid entry and E for a masked one, and
+// entry position p = t*K + k:
+//   packed layout: row  = #{p' : (key', p') < (key, p)} (lexicographic), the
+//                  stable counting sort by expert;
+//   padded layout: rank = #{p' < p : key' == key}, row = key*capacity + rank,
+//                  dropped when rank >= capacity.
+// Encoding an entry as key*n + p turns the packed count into one integer
+// comparison per entry, and the padded rank into the difference of two
+// such counts (entries with code below key*n are exactly those of a smaller
+// key).  Each wavefront compares 64 entries per step against its token's
+// K codes and counts the matches with a ballot and a popcount, so the
+// counts stay wave-uniform and only the four per-wave totals meet, in LDS.
+// Integer counting is exact and order-free: the result is a pure function
+// of topk_idx.
+//
+// Work split: workgroup 0 histograms all entries with LDS atomic adds and
+// writes counts (and, packed, the exclusive-scan offsets).  Every other
+// workgroup owns 256 work items of one token (16 channels each for FP8, 8 for
+// BF16, as in the dispatch kernel).  It issues the token loads first, so
+// they overlap the counting, then finds the token's K rows.  The first
+// workgroup of a token writes the token's slot and src entries.  Then every
+// workgroup writes its part of the K receive rows.  Every workgroup reads
+// all n ids (4n bytes, from L2 after the first) and compares them with its
+// token's K codes, so the counting grows as n*K per workgroup.  On MI355X
+// (256 experts, top-8, hidden 7168) one launch takes 6.4 us against 3.8 +
+// 4.8 us for the two kernels at 1024 entries, 9.0 against 11.6 us at 2048,
+// and breaks even at 3072; the path is used up to 3072 entries, and larger
+// batches run the layout kernels and the dispatch kernel.
+
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxK = 32;
+static_assert(static_cast<int64_t>(1025) * kFusedMaxEntries < (int64_t(1) << 31), "entry codes fit int32");
+
+// LDS: workgroup 0 needs E+1 histogram bins and the scan's wave totals; the
+// token workgroups need the per-wave counts, the K rows and the K keys.
+constexpr int kTokenLdsInts = 2 * kWaves * kMaxK + 2 * kMaxK;
+constexpr int kLdsInts = 1025 + kWaves > kTokenLdsInts ? 1025 + kWaves : kTokenLdsInts;
+
+__device__ __forceinline__ int key_of(int e, int E) { return (e >= 0 && e < E) ? e : E; }
+
+// This lane's ids: entries u*256 + tid for u < NS, with the address clamped
+// to the last entry (n >= 1) so that all NS loads are issued back to back,
+// free of branches; lanes past n get a copy of the last id, which callers
+// mask by position.
+template <int NS>
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int n, int (&e)[NS]) {
+#pragma unroll
+  for (int u = 0; u < NS; ++u) e[u] = idx[min(u * kThreads + static_cast<int>(threadIdx.x), n - 1)];
+}
+
+// Workgroup 0: per-expert counts (clamped to the capacity in the padded
+// layout) and, for the packed layout, the exclusive-scan offsets.
+template <int NS>
+__device__ void write_counts_block(const int32_t* __restrict__ idx, int n, int E, int cap, int* lds,
+                                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  const int tid = threadIdx.x, nk = E + 1;
+  int* hist = lds;
+  int* wave_tot = lds + nk;
+  int e[NS];
+  if (n > 0) load_ids<NS>(idx, n, e);  // block-uniform; nothing to read for an empty batch
+  for (int i = tid; i < nk; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  if (n > 0) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+      if (u * kThreads + tid < n) atomicAdd(&hist[key_of(e[u], E)], 1);
+  }
+  __syncthreads();
+  for (int j = tid; j < E; j += kThreads) counts[j] = cap == 0 ? hist[j] : min(hist[j], cap);
+  if (cap == 0) {  // block-uniform
+    block_exclusive_scan(hist, nk, wave_tot);
+    for (int j = tid; j <= E; j += kThreads) offsets[j] = hist[j];
+  }
+}
+
+// Per-wave counts for targets k0 .. k0+KC-1 (expert ids te) of the token
+// whose entries start at p0: below[j] = #{entries with code < code_j} and,
+// padded, under[j] = #{entries with code < key_j * n}.  `code` holds this
+// lane's entry codes (INT_MAX past n); the wave's entries are
+// lane + 64*w + 256*u.  Lane 0 of each wave leaves its counts in LDS, and
+// wave 0 the targets' keys.
+template <int KC, int NS>
+__device__ __forceinline__ void count_targets(const int (&te)[KC], int p0, int k0, int K, int n, int E, bool padded,
+                                              const int (&code)[NS], int nsteps, int* wc_below, int* wc_under,
+                                              int* tkey) {
+  int tk[KC], tcode[KC], tlow[KC];
+#pragma unroll
+  for (int j = 0; j < KC; ++j) {
+    tk[j] = k0 + j < K ? key_of(te[j], E) : E;
+    tcode[j] = tk[j] * n + p0 + k0 + j;
+    tlow[j] = tk[j] * n;
+  }
+  int below[KC], under[KC];
+#pragma unroll
+  for (int j = 0; j < KC; ++j) below[j] = under[j] = 0;
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    if (u >= nsteps) break;  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      below[j] += __popcll(wave_ballot(code[u] < tcode[j]));
+      if (padded) under[j] += __popcll(wave_ballot(code[u] < tlow[j]));
+    }
+  }
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      if (k0 + j >= K) break;
+      wc_below[w * kMaxK + k0 + j] = below[j];
+      wc_under[w * kMaxK + k0 + j] = under[j];
+      if (w == 0) tkey[k0 + j] = tk[j];
+    }
+  }
+}
+
+// NS: 256-entry steps per lane (n <= NS*256).
+template <int KT, bool FP8, int NS>
+__global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, const float* __restrict__ w, int32_t T,
+    int32_t H, int32_t Krt, int32_t E, int32_t cap, uint32_t nchunk, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src, void* __restrict__ recv,
+    float* __restrict__ recv_scale, float* __restrict__ recv_weight) {
+  __shared__ int lds[kLdsInts];
+  constexpr int KC = KT > 0 ? KT : 8;  // targets counted per pass over the ids
+  const int K = KT > 0 ? KT : Krt;
+  const int n = T * K;
+  if (blockIdx.x == 0) {
+    write_counts_block<NS>(idx, n, E, cap, lds, counts, offsets);
+    return;
+  }
+  const uint32_t b = blockIdx.x - 1;
+  const int t = static_cast<int>(b / nchunk);
+  const uint32_t chunk = b - static_cast<uint32_t>(t) * nchunk;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const uint32_t vpt = static_cast<uint32_t>(H) / (FP8 ? 16 : 8);
+  const uint32_t v = chunk * kThreads + tid;  // vector within the token
+  const bool active = v < vpt;
+  const int p0 = t * K;
+
+  // every load up front: the token's expert ids, the token itself (its
+  // latency overlaps the counting), then all ids
+  int te[KC];
+#pragma unroll
+  for (int j = 0; j < KC; ++j) te[j] = idx[p0 + min(j, K - 1)];
+  u32x4 a = {0, 0, 0, 0}, a2 = {0, 0, 0, 0};
+  if (active) {
+    const u32x4* px = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * H);
+    if (FP8) {
+      a = __builtin_nontemporal_load(px + 2 * v);
+      a2 = __builtin_nontemporal_load(px + 2 * v + 1);
+    } else {
+      a = __builtin_nontemporal_load(px + v);
+    }
+  }
+  int code[NS];
+  load_ids<NS>(idx, n, code);
+  // keep every load above this point: the compiler would otherwise sink
+  // some of them next to their first use, one memory latency after another
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int p = u * kThreads + wv * kWave + lane;
+    code[u] = p < n ? key_of(code[u], E) * n + p : 0x7FFFFFFF;
+  }
+
+  const int nsteps = (n + kThreads - 1) / kThreads;
+  int* wc_below = lds;                   // [kWaves][kMaxK]
+  int* wc_under = lds + kWaves * kMaxK;  // [kWaves][kMaxK]
+  int* rows = lds + 2 * kWaves * kMaxK;  // [kMaxK]
+  int* tkey = rows + kMaxK;              // [kMaxK]
+  const bool padded = cap > 0;
+  count_targets<KC, NS>(te, p0, 0, K, n, E, padded, code, nsteps, wc_below, wc_under, tkey);
+  for (int k0 = KC; k0 < K; k0 += KC) {  // top-k beyond one pass (generic K only)
+#pragma unroll
+    for (int j = 0; j < KC; ++j) te[j] = idx[p0 + min(k0 + j, K - 1)];
+    count_targets<KC, NS>(te, p0, k0, K, n, E, padded, code, nsteps, wc_below, wc_under, tkey);
+  }
+  __syncthreads();
+
+  // lanes 0..K-1 turn the counts into rows while every lane quantises
+  if (tid < K) {
+    int below = 0, under = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      below += wc_below[ww * kMaxK + tid];
+      under += wc_under[ww * kMaxK + tid];
+    }
+    const int k = tkey[tid];
+    const bool valid = k < E;
+    int row;
+    if (!padded) {
+      row = valid ? below : -1;
+      if (chunk == 0) {
+        slot[p0 + tid] = row;
+        src[below] = valid ? t : -1;  // masked entries take the rows after the valid ones
+      }
+    } else {
+      const int rank = below - under;
+      row = (valid && rank < cap) ? k * cap + rank : -1;
+      if (chunk == 0) {
+        slot[p0 + tid] = row;
+        if (row >= 0) src[row] = t;
+      }
+    }
+    rows[tid] = row;
+  }
+  float s = 1.0f;
+  u32x4 q = a;
+  if (FP8) q = quantize16_e4m3(a, a2, s);
+  __syncthreads();
+  if (!active) return;
+
+  const bool want_w = recv_weight != nullptr && v == 0;
+  const float* wrow = w != nullptr ? w + static_cast<size_t>(p0) : nullptr;
+  const uint32_t G = static_cast<uint32_t>(H) / kGroup;
+  const bool lead = (v & 7) == 0;  // one lane per group writes the scale
+#pragma unroll
+  for (int k = 0; k < (KT > 0 ? KT : kMaxK); ++k) {
+    if (k >= K) break;
+    const int r = rows[k];
+    if (r < 0) continue;
+    if (FP8) {
+      reinterpret_cast<u32x4*>(static_cast<uint8_t*>(recv) + static_cast<size_t>(r) * H)[v] = q;
+      if (lead) recv_scale[static_cast<size_t>(r) * G + (v >> 3)] = s;
+    } else {
+      reinterpret_cast<u32x4*>(static_cast<uint16_t*>(recv) + static_cast<size_t>(r) * H)[v] = q;
+    }
+    if (want_w) recv_weight[r] = wrow[k];
+  }
+}
+
+template <bool FP8, int NS>
+void launch_fused(const int32_t* idx, const uint16_t* x, const float* w, int32_t T, int32_t H, int32_t K,
+                  int32_t E, int32_t cap, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
+                  void* recv, float* recv_scale, float* recv_weight, hipStream_t stream) {
+  const uint32_t vpt = static_cast<uint32_t>(H) / (FP8 ? 16 : 8);
+  const uint32_t nchunk = (vpt + kThreads - 1) / kThreads;
+  const dim3 grid(1 + static_cast<uint32_t>(T) * nchunk), block(kThreads);
+#define EP_FUSED(KV)                                                                                            \
+  hipLaunchKernelGGL((layout_dispatch_kernel<KV, FP8, NS>), grid, block, 0, stream, idx, x, w, T, H, K, E, cap, \
+                     nchunk, counts, offsets, slot, src, recv, recv_scale, recv_weight)
+  switch (K) {
+    case 1: EP_FUSED(1); break;
+    case 2: EP_FUSED(2); break;
+    case 4: EP_FUSED(4); break;
+    case 6: EP_FUSED(6); break;
+    case 8: EP_FUSED(8); break;
+    default: EP_FUSED(0); break;
+  }
+#undef EP_FUSED
+}
+
+template <bool FP8>
+void launch_fused_ns(const int32_t* idx, const uint16_t* x, const float* w, int32_t T, int32_t H, int32_t K,
+                     int32_t E, int32_t cap, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
+                     void* recv, float* recv_scale, float* recv_weight, hipStream_t stream) {
+  const int n = T * K;
+  static_assert(kFusedMaxEntries <= 12 * kThreads, "steps per lane");
+  if (n <= 4 * kThreads)
+    launch_fused<FP8, 4>(idx, x, w, T, H, K, E, cap, counts, offsets, slot, src, recv, recv_scale, recv_weight,
+                         stream);
+  else if (n <= 8 * kThreads)
+    launch_fused<FP8, 8>(idx, x, w, T, H, K, E, cap, counts, offsets, slot, src, recv, recv_scale, recv_weight,
+                         stream);
+  else
+    launch_fused<FP8, 12>(idx, x, w, T, H, K, E, cap, counts, offsets, slot, src, recv, recv_scale, recv_weight,
+                          stream);
+}
+
+}  // namespace
+
+hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, const float* topk_weights,
+                                  int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
+                                  int32_t capacity, bool fp8, int32_t* counts, int32_t* offsets, int32_t* slot,
+                                  int32_t* src, void* recv, float* recv_scale, float* recv_weight,
+                                  void* workspace, hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>(num_tokens) * top_k;
+  if (n > kFusedMaxEntries) {
+    hipError_t e = launch_layout(topk_idx, static_cast<int32_t>(n), top_k, num_experts, capacity, counts, offsets,
+                                 slot, src, workspace, stream);
+    if (e != hipSuccess) return e;
+    return fp8 ? launch_dispatch_fp8(x, num_tokens, hidden, top_k, slot, topk_weights, static_cast<uint8_t*>(recv),
+                                     recv_scale, recv_weight, stream)
+               : launch_dispatch_bf16(x, num_tokens, hidden, top_k, slot, topk_weights,
+                                      static_cast<uint16_t*>(recv), recv_weight, stream);
+  }
+  if (fp8)
+    launch_fused_ns<true>(topk_idx, x, topk_weights, num_tokens, hidden, top_k, num_experts, capacity, counts,
+                          offsets, slot, src, recv, recv_scale, recv_weight, stream);
+  else
+    launch_fused_ns<false>(topk_idx, x, topk_weights, num_tokens, hidden, top_k, num_experts, capacity, counts,
+                           offsets, slot, src, recv, recv_scale, recv_weight, stream);
+  return hipGetLastError();
+}
+
+}  // namespace ep

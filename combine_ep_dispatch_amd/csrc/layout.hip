@@ -45,43 +45,6 @@ constexpr int kFusedMaxEntries = 65536;   // one launch, no workspace
 constexpr int kMultiThreads = 256;
 constexpr int kMultiWaves = kMultiThreads / kWave;
 
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
-
-// Exclusive prefix sum of data[0..n) in LDS, in place.  Every thread of the
-// block must call it.  wave_tot needs blockDim.x / 64 ints of LDS.
-__device__ void block_exclusive_scan(int* data, int n, int* wave_tot) {
-  const int tid = threadIdx.x, bs = blockDim.x;
-  const int lane = tid & (kWave - 1), w = tid / kWave, nw = bs / kWave;
-  const int per = (n + bs - 1) / bs;
-  const int beg = min(n, tid * per), end = min(n, beg + per);
-  int local = 0;
-  for (int i = beg; i < end; ++i) local += data[i];
-  const int incl = wave_inclusive_scan(local);
-  if (lane == kWave - 1) wave_tot[w] = incl;
-  __syncthreads();
-  if (w == 0) {
-    const int v = lane < nw ? wave_tot[lane] : 0;
-    const int s = wave_inclusive_scan(v);
-    if (lane < nw) wave_tot[lane] = s - v;
-  }
-  __syncthreads();
-  int run = wave_tot[w] + incl - local;
-  for (int i = beg; i < end; ++i) {
-    const int c = data[i];
-    data[i] = run;
-    run += c;
-  }
-  __syncthreads();
-}
-
 // Rank ITERS consecutive 64-entry steps of this wavefront: entries
 // [p_begin, p_end).  lmask (E+1 lane masks, all zero on entry and on exit)
 // and cnt (E+1 running counts) are this wave's LDS rows.  On return key[i]

@@ -3,7 +3,8 @@
 A serving loop calls layout -> dispatch -> combine on the same buffers every
 step.  ``StepPlan`` checks dtypes, shapes and devices once, allocates the
 layout workspace once and caches raw pointers and the stream handle, so a
-step costs three plain C calls (which still validate their arguments).
+step costs two plain C calls, layout+dispatch and combine (which still
+validate their arguments).
 The kernels are the same ones the ``ep_*`` functions launch.
 """
 
@@ -70,6 +71,12 @@ class StepPlan:
                                self.stream)
         self._combine_args = (self.y.data_ptr(), self.slot.data_ptr(), topk_weights.data_ptr(), T, H, K,
                               self.out.data_ptr(), self.stream)
+        ws = self.workspace
+        self._layout_dispatch_args = (
+            topk_idx.data_ptr(), x.data_ptr(), None, T, H, K, E, self.capacity, self.fmt, self.counts.data_ptr(),
+            None if self.capacity else self.offsets.data_ptr(), self.slot.data_ptr(), self.src.data_ptr(),
+            self.recv_x.data_ptr(), self.recv_scale.data_ptr() if self.recv_scale is not None else None, None,
+            ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, self.stream)
 
     def _make_layout_args(self):
         ws = self.workspace
@@ -92,10 +99,13 @@ class StepPlan:
     def dispatch(self):
         check("ep_dispatch", LIB.ep_dispatch(*self._dispatch_args))
 
+    def layout_dispatch(self):
+        """layout() and dispatch() as one call (one launch up to 3072 entries)."""
+        check("ep_layout_dispatch", LIB.ep_layout_dispatch(*self._layout_dispatch_args))
+
     def combine(self):
         check("ep_combine", LIB.ep_combine(*self._combine_args))
 
     def step(self):
-        self.layout()
-        self.dispatch()
+        self.layout_dispatch()
         self.combine()

@@ -64,8 +64,8 @@ typedef enum {
 /* Human-readable name of a status code (static storage). */
 const char* ep_status_string(int status);
 
-/* Bytes of device workspace ep_dispatch_layout and ep_dispatch_layout_padded
- * need for this shape: 0 up to 65536 entries (T*K), which one launch
+/* Bytes of device workspace ep_dispatch_layout, ep_dispatch_layout_padded
+ * and ep_layout_dispatch need for this shape: 0 up to 65536 entries (T*K), which one launch
  * handles; beyond, (E+1) int32 per 4096-entry chunk.  Pure host function. */
 size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t top_k, int32_t num_experts);
 
@@ -160,6 +160,35 @@ ep_status ep_dispatch_layout_padded(const int32_t* topk_idx, int64_t num_tokens,
 ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, int32_t top_k,
                       const int32_t* slot, const float* topk_weights, int32_t format,
                       void* recv_x, float* recv_scale, float* recv_weight, void* stream);
+
+/*
+ * ep_layout_dispatch - layout and dispatch in one call, the shape of the
+ * pages' dispatch call, which takes the tokens with their routing and
+ * returns the received rows together with the handle ([P4 "使用示例 › MoE
+ * 训练中的应用"]), or, with capacity > 0, fills per-expert buffers and
+ * reports per-expert counts ([P4 "使用示例 › 推理解码阶段的应用"]).
+ *
+ * Writes exactly what ep_dispatch_layout (capacity == 0) or
+ * ep_dispatch_layout_padded (capacity > 0) followed by ep_dispatch would
+ * write, bit for bit.  Up to 3072 entries (T*K) this is one kernel launch
+ * (the decode sizes, where launch latency dominates); beyond, the same
+ * launches as the separate calls.
+ *
+ * topk_idx, tokens_per_expert, slot, src_token, workspace: as for
+ *   ep_dispatch_layout (capacity == 0) or ep_dispatch_layout_padded
+ *   (capacity > 0, where tokens_per_expert receives recv_expert_count);
+ * expert_offset int32 [E+1] out for capacity == 0; unused and may be NULL
+ *   for capacity > 0;
+ * x, topk_weights, format, recv_x, recv_scale, recv_weight: as for
+ *   ep_dispatch, with rows = T*K (capacity == 0) or E*capacity.
+ * Requirements: the union of those calls' requirements.
+ */
+ep_status ep_layout_dispatch(const int32_t* topk_idx, const void* x, const float* topk_weights,
+                             int64_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
+                             int32_t capacity, int32_t format, int32_t* tokens_per_expert,
+                             int32_t* expert_offset, int32_t* slot, int32_t* src_token, void* recv_x,
+                             float* recv_scale, float* recv_weight, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * ep_combine - reduce each token's K expert outputs back to the token.

@@ -136,3 +136,33 @@ def test_step_plan_rejects_host_tensors():
     x = torch.zeros((4, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU device"):
         ep.StepPlan(idx, w, x, 8)
+
+
+def test_layout_dispatch_rejects_bad_arguments(lib):
+    """ep_layout_dispatch checks the union of the layout and dispatch
+    arguments; every call below fails validation before any launch."""
+    F = lib.LIB.ep_layout_dispatch
+    fp8, bf16 = lib.EP_RECV_FP8_E4M3_G128, lib.EP_RECV_BF16
+    ok = dict(idx=FAKE, x=FAKE, w=None, T=4, H=256, K=2, E=8, cap=0, fmt=fp8, c=FAKE, o=FAKE, s=FAKE, r=FAKE,
+              rx=FAKE, rs=FAKE, rw=None, ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return F(a["idx"], a["x"], a["w"], a["T"], a["H"], a["K"], a["E"], a["cap"], a["fmt"], a["c"], a["o"],
+                 a["s"], a["r"], a["rx"], a["rs"], a["rw"], a["ws"], a["wsb"], None)
+
+    bad = lib.EP_ERR_INVALID_ARG
+    assert call(K=0) == bad and call(T=-1) == bad and call(E=0) == bad and call(cap=-1) == bad
+    assert call(E=1025) == lib.EP_ERR_UNSUPPORTED and call(K=33) == lib.EP_ERR_UNSUPPORTED
+    assert call(o=None) == bad                       # packed layout needs offsets
+    assert call(cap=4, r=None) == bad                # padded layout needs src
+    assert call(cap=1 << 21, E=1024) == bad          # E*cap >= 2**31
+    assert call(c=None) == bad and call(idx=None) == bad and call(s=FAKE + 2) == bad
+    assert call(H=200) == bad                        # FP8 needs H % 128 == 0
+    assert call(H=130, fmt=bf16) == bad              # H % 8
+    assert call(fmt=7) == bad
+    assert call(rs=None) == bad                      # FP8 needs the scales
+    assert call(x=FAKE + 8) == bad                   # 16-byte alignment
+    assert call(rw=FAKE) == bad                      # recv_weight needs topk_weights
+    assert call(T=8200, K=8, E=256) == bad           # past 65536 entries the workspace is required
+    assert call(T=1 << 20, K=8) == lib.EP_ERR_UNSUPPORTED

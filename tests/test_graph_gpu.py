@@ -10,12 +10,14 @@ from workloads import make_workload
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,capacity", [("decode", 0), ("decode", 128), ("prefill", 0)])
-def test_graph_replays_match_eager(gpu, name, capacity):
+@pytest.mark.parametrize("name,capacity,fused", [("decode", 0, False), ("decode", 128, False), ("prefill", 0, False),
+                                                ("decode", 0, True), ("decode", 128, True)])
+def test_graph_replays_match_eager(gpu, name, capacity, fused):
+    """fused: layout and dispatch through the one ep_layout_dispatch call."""
     ep = gpu
     wl = make_workload(name, seed=4)
     T, H, E, K = wl.T, wl.H, wl.E, wl.K
-    print("case graph", name, capacity, flush=True)
+    print("case graph", name, capacity, fused, flush=True)
     dev = "cuda"
     idx = torch.from_numpy(wl.topk_idx).to(dev)
     w = torch.from_numpy(wl.topk_weights).to(dev)
@@ -33,11 +35,15 @@ def test_graph_replays_match_eager(gpu, name, capacity):
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     def step():
-        if capacity:
-            ep.ep_dispatch_layout_padded(idx, E, capacity, counts, slot, src, ws)
+        if fused:
+            ep.ep_layout_dispatch(idx, x, None, E, capacity, ep.EP_RECV_FP8_E4M3_G128, counts,
+                                  None if capacity else offsets, slot, src, recv, scale, None, ws)
         else:
-            ep.ep_dispatch_layout(idx, E, counts, offsets, slot, src, ws)
-        ep.ep_dispatch(x, slot, None, ep.EP_RECV_FP8_E4M3_G128, recv, scale, None, num_rows=R)
+            if capacity:
+                ep.ep_dispatch_layout_padded(idx, E, capacity, counts, slot, src, ws)
+            else:
+                ep.ep_dispatch_layout(idx, E, counts, offsets, slot, src, ws)
+            ep.ep_dispatch(x, slot, None, ep.EP_RECV_FP8_E4M3_G128, recv, scale, None, num_rows=R)
         ep.ep_combine(y, slot, w, out, num_rows=R)
 
     step()

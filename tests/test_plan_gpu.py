@@ -12,13 +12,16 @@ from workloads import make_workload, to_bf16_bits
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("separate", [False, True])
 @pytest.mark.parametrize("name,T,capacity,fp8", [("decode", None, 0, True), ("decode", None, 128, True),
                                                  ("decode", None, 0, False), ("tiny", None, 3, True),
                                                  ("skew", 9000, 0, True), ("prefill", None, 0, True)])
-def test_step_plan_matches_oracle(gpu, name, T, capacity, fp8):
+def test_step_plan_matches_oracle(gpu, name, T, capacity, fp8, separate):
+    """separate: layout(), dispatch(), combine() as three calls instead of
+    step() (layout and dispatch in one call, then combine)."""
     ep = gpu
     wl = make_workload(name, seed=7, T=T)
-    print("case plan", name, wl.T, capacity, fp8, flush=True)
+    print("case plan", name, wl.T, capacity, fp8, separate, flush=True)
     idx = torch.from_numpy(wl.topk_idx).cuda()
     w = torch.from_numpy(wl.topk_weights).cuda()
     x = torch.from_numpy(wl.x_bits.view(np.int16)).cuda()
@@ -28,7 +31,12 @@ def test_step_plan_matches_oracle(gpu, name, T, capacity, fp8):
     y = to_bf16_bits(rng.standard_normal((rows, wl.H), dtype=np.float32))
     plan.y.copy_(torch.from_numpy(y.view(np.int16)).cuda().view(torch.bfloat16))
     for _ in range(2):  # the second step reuses every buffer
-        plan.step()
+        if separate:
+            plan.layout()
+            plan.dispatch()
+            plan.combine()
+        else:
+            plan.step()
     if capacity:
         oc, oslot, osrc = oracle.dispatch_layout_padded(wl.topk_idx, wl.E, capacity)
         assert np.array_equal(host(plan.counts), oc)
