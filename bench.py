@@ -15,7 +15,8 @@ are seeded synthetic tensors already resident in HBM when timing starts.
 The JSON line reports throughput as algorithmic bytes per second (bytes the
 method must move, every one of the K copies counted), the per-kernel
 launch durations measured with HIP events on the launch stream, the
-roofline of the dominant kernel (combine), the decode-size (128 tokens)
+roofline of the dominant kernel (combine), p10 / median / p90 of single
+steps warm and with the Infinity Cache flushed before each, the decode-size (128 tokens)
 step time (eager launches through the checked binding and through
 StepPlan, and as a replayed HIP graph, packed and with the low-latency
 padded layout), the backward helpers at the prefill size, and
@@ -189,6 +190,45 @@ def time_steps(torch, s, steps, warmup):
     return us_step, {k: sum(v) / len(v) for k, v in per.items()}, wall
 
 
+def time_distribution(torch, s, reps, flush_bytes=0):
+    """Per-step and per-kernel durations over `reps` steps, each step timed
+    on its own with HIP events between the three calls (launch stream).
+    flush_bytes > 0: before every step a device fill of that many bytes
+    (outside the timed region) evicts the 256 MB Infinity Cache, so the
+    step starts from HBM.  Returns {name: {"p10", "median", "p90"}} in µs."""
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    for _ in range(3):
+        s.step()
+    torch.cuda.synchronize()
+    marks = []
+    for _ in range(reps):
+        if scratch is not None:
+            scratch.fill_(1)
+        m = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        m[0].record(stream)
+        s.layout()
+        m[1].record(stream)
+        s.dispatch()
+        m[2].record(stream)
+        s.combine()
+        m[3].record(stream)
+        marks.append(m)
+    torch.cuda.synchronize()
+    series = {"step": [m[0].elapsed_time(m[3]) * 1e3 for m in marks],
+              "layout": [m[0].elapsed_time(m[1]) * 1e3 for m in marks],
+              "dispatch": [m[1].elapsed_time(m[2]) * 1e3 for m in marks],
+              "combine": [m[2].elapsed_time(m[3]) * 1e3 for m in marks]}
+    del scratch
+
+    def pct(v, q):
+        v = sorted(v)
+        return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
+    return {k: {"p10": round(pct(v, 0.1), 2), "median": round(pct(v, 0.5), 2), "p90": round(pct(v, 0.9), 2)}
+            for k, v in series.items()}
+
+
 def time_loop(torch, fn, steps, warmup):
     """Mean µs of fn over `steps` back-to-back calls, HIP events only at the
     ends (on the launch stream)."""
@@ -283,7 +323,14 @@ def cpu_baseline(wl, budget_s):
             oracle.combine(y_chunk, sub_slot[:n], wl.topk_weights[t:t + n])
         passes += 1
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(passes * step_b / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": "%d full pass(es) of the same 4096-token workload (layout, FP8 dispatch and combine of "
                       "every token in 512-token chunks), %.1f s, numpy single-threaded; %d host CPUs visible"
                       % (passes, dt, os.cpu_count())}
@@ -489,6 +536,7 @@ def main():
     total_b = lay_b + dis_b + com_b
     gbs = total_b / (us_step * 1e-6) / 1e9
     graph_us = time_graph(torch, s.step, 50)
+    dist = {"warm": time_distribution(torch, s, 50), "flushed": time_distribution(torch, s, 50, 512 << 20)}
     s.backward_buffers(torch)
     db_b, cb_b = backward_bytes(s.wl.T, s.wl.H, s.wl.K)
     db_us = time_calls(torch, s.dispatch_backward, 30)
@@ -535,6 +583,9 @@ def main():
         "us_per_step_graph": round(graph_us, 2),
         "kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "kernel_alg_bytes": {"layout": lay_b, "dispatch": dis_b, "combine": com_b},
+        "step_distribution_us": dict(dist, note="50 steps each timed alone (events between the calls); flushed: "
+                                                "a 512 MB device fill before every step evicts the Infinity Cache"),
+        "flushed_GBs_at_median": round(total_b / dist["flushed"]["step"]["median"] / 1e3, 1),
         "decode_128tok_us": dict(decode[0], low_latency_padded_128=decode[128]),
         "backward_us": {"dispatch_backward": round(db_us, 2), "combine_backward": round(cb_us, 2),
                         "dispatch_backward_GBs": round(db_b / db_us / 1e3, 1),
