@@ -193,18 +193,21 @@ def time_steps(torch, s, steps, warmup):
 def time_distribution(torch, s, reps, flush_bytes=0):
     """Per-step and per-kernel durations over `reps` steps, each step timed
     on its own with HIP events between the three calls (launch stream).
-    flush_bytes > 0: before every step a device fill of that many bytes
-    (outside the timed region) evicts the 256 MB Infinity Cache, so the
-    step starts from HBM.  Returns {name: {"p10", "median", "p90"}} in µs."""
+    flush_bytes > 0: before every step a device read of that many bytes (a
+    reduction, outside the timed region) evicts the 256 MB Infinity Cache,
+    so the step starts from HBM.  A write fill would evict it too, but
+    leaves that many dirty lines whose write-back then slows the next
+    kernel (measured: the dispatch kernel 66 µs instead of 54).  Returns
+    {name: {"p10", "median", "p90"}} in µs."""
     stream = torch.cuda.current_stream()
-    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    scratch = torch.ones(flush_bytes // 4, dtype=torch.int32, device="cuda") if flush_bytes else None
     for _ in range(3):
         s.step()
     torch.cuda.synchronize()
     marks = []
     for _ in range(reps):
         if scratch is not None:
-            scratch.fill_(1)
+            scratch.max()
         m = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         m[0].record(stream)
         s.layout()
@@ -584,7 +587,7 @@ def main():
         "kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "kernel_alg_bytes": {"layout": lay_b, "dispatch": dis_b, "combine": com_b},
         "step_distribution_us": dict(dist, note="50 steps each timed alone (events between the calls); flushed: "
-                                                "a 512 MB device fill before every step evicts the Infinity Cache"),
+                                                "a 512 MB device read before every step evicts the Infinity Cache"),
         "flushed_GBs_at_median": round(total_b / dist["flushed"]["step"]["median"] / 1e3, 1),
         "decode_128tok_us": dict(decode[0], low_latency_padded_128=decode[128]),
         "backward_us": {"dispatch_backward": round(db_us, 2), "combine_backward": round(cb_us, 2),
