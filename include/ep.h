@@ -15,7 +15,8 @@
  * permutation into an expert-major receive buffer in the same HBM, and the
  * handle is the routing layout below.  The pages' single dispatch call is
  * split into ep_dispatch_layout (routing metadata) and ep_dispatch (the
- * data movement); ep_combine is the reduction.
+ * data movement), and is also offered whole as ep_layout_dispatch;
+ * ep_combine is the reduction.
  *
  * Conventions for every call
  *   - All array arguments are DEVICE pointers to contiguous row-major

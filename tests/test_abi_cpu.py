@@ -166,3 +166,23 @@ def test_layout_dispatch_rejects_bad_arguments(lib):
     assert call(rw=FAKE) == bad                      # recv_weight needs topk_weights
     assert call(T=8200, K=8, E=256) == bad           # past 65536 entries the workspace is required
     assert call(T=1 << 20, K=8) == lib.EP_ERR_UNSUPPORTED
+
+
+def test_header_is_strict_c():
+    """include/ep.h is a C header: it compiles as strict C99 on its own."""
+    import subprocess
+    r = subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-x", "c",
+                        HEADER], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_c_driver_compiles_and_links(lib, tmp_path):
+    """The plain-C test driver builds against include/ep.h and links every
+    call it makes against libep.so."""
+    import importlib.util
+    import subprocess
+    spec = importlib.util.spec_from_file_location("_c_abi_build", os.path.join(ROOT, "tests", "c_abi", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    r = subprocess.run(mod.command(str(tmp_path / "ep_step")), capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
