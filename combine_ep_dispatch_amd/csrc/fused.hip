@@ -15,10 +15,10 @@
 //                  stable counting sort by expert;
 //   padded layout: rank = #{p' < p : key' == key}, row = key*capacity + rank,
 //                  dropped when rank >= capacity.
-// Encoding an entry as key*n + p turns the packed count into one integer
-// comparison per entry, and the padded rank into the difference of two
-// such counts (entries with code below key*n are exactly those of a smaller
-// key).  Each wavefront compares 64 entries per step against its token's
+// Encoding an entry as key*n + p turns either count into one integer range
+// test per entry: the packed row counts codes below the entry's own, the
+// padded rank the codes from key*n up to it (entries with a code below
+// key*n are exactly those of a smaller key).  Each wavefront compares 64 entries per step against its token's
 // K codes and counts the matches with a ballot and a popcount, so the
 // counts stay wave-uniform and only the four per-wave totals meet, in LDS.
 // Integer counting is exact and order-free: the result is a pure function
@@ -26,17 +26,19 @@
 //
 // Work split: workgroup 0 histograms all entries with LDS atomic adds and
 // writes counts (and, packed, the exclusive-scan offsets).  Every other
-// workgroup owns 256 work items of one token (16 channels each for FP8, 8 for
-// BF16, as in the dispatch kernel).  It issues the token loads first, so
+// workgroup owns the work items of one token (16 channels each for FP8, 8
+// for BF16, as in the dispatch kernel; a token wider than 1024 items is
+// split over several workgroups).  It issues the token loads first, so
 // they overlap the counting, then finds the token's K rows.  The first
 // workgroup of a token writes the token's slot and src entries.  Then every
 // workgroup writes its part of the K receive rows.  Every workgroup reads
 // all n ids (4n bytes, from L2 after the first) and compares them with its
 // token's K codes, so the counting grows as n*K per workgroup.  On MI355X
-// (256 experts, top-8, hidden 7168) one launch takes 6.4 us against 3.8 +
-// 4.8 us for the two kernels at 1024 entries, 9.0 against 11.6 us at 2048,
-// and breaks even at 3072; the path is used up to 3072 entries, and larger
-// batches run the layout kernels and the dispatch kernel.
+// (256 experts, top-8, hidden 7168) one launch takes 6.4 us against 4.0 +
+// 4.9 us for the two kernels at 1024 entries, 8.6 against 11.4 us at 2048
+// and 10.9 against 12.6 us at 3072, and breaks even at 4096; the path is
+// used up to 3072 entries, and larger batches run the layout kernels and
+// the dispatch kernel.
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -44,26 +46,28 @@
 namespace ep {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kMinThreads = 256;   // a workgroup has 256..1024 lanes, a multiple of 64
+constexpr int kMaxThreads = 1024;
+constexpr int kMaxWaves = kMaxThreads / kWave;
 constexpr int kMaxK = 32;
 static_assert(static_cast<int64_t>(1025) * kFusedMaxEntries < (int64_t(1) << 31), "entry codes fit int32");
 
 // LDS: workgroup 0 needs E+1 histogram bins and the scan's wave totals; the
 // token workgroups need the per-wave counts, the K rows and the K keys.
-constexpr int kTokenLdsInts = 2 * kWaves * kMaxK + 2 * kMaxK;
-constexpr int kLdsInts = 1025 + kWaves > kTokenLdsInts ? 1025 + kWaves : kTokenLdsInts;
+constexpr int kTokenLdsInts = kMaxWaves * kMaxK + 2 * kMaxK;
+constexpr int kLdsInts = 1025 + kMaxWaves > kTokenLdsInts ? 1025 + kMaxWaves : kTokenLdsInts;
 
 __device__ __forceinline__ int key_of(int e, int E) { return (e >= 0 && e < E) ? e : E; }
 
-// This lane's ids: entries u*256 + tid for u < NS, with the address clamped
-// to the last entry (n >= 1) so that all NS loads are issued back to back,
-// free of branches; lanes past n get a copy of the last id, which callers
-// mask by position.
+// This lane's ids: entries u*blockDim + tid for u < NS, with the address
+// clamped to the last entry (n >= 1) so that all NS loads are issued back
+// to back, free of branches; lanes past n get a copy of the last id, which
+// callers mask by position.
 template <int NS>
 __device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int n, int (&e)[NS]) {
+  const int bs = blockDim.x;
 #pragma unroll
-  for (int u = 0; u < NS; ++u) e[u] = idx[min(u * kThreads + static_cast<int>(threadIdx.x), n - 1)];
+  for (int u = 0; u < NS; ++u) e[u] = idx[min(u * bs + static_cast<int>(threadIdx.x), n - 1)];
 }
 
 // Workgroup 0: per-expert counts (clamped to the capacity in the padded
@@ -71,70 +75,68 @@ __device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int n,
 template <int NS>
 __device__ void write_counts_block(const int32_t* __restrict__ idx, int n, int E, int cap, int* lds,
                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  const int tid = threadIdx.x, nk = E + 1;
+  const int tid = threadIdx.x, bs = blockDim.x, nk = E + 1;
   int* hist = lds;
   int* wave_tot = lds + nk;
   int e[NS];
   if (n > 0) load_ids<NS>(idx, n, e);  // block-uniform; nothing to read for an empty batch
-  for (int i = tid; i < nk; i += kThreads) hist[i] = 0;
+  for (int i = tid; i < nk; i += bs) hist[i] = 0;
   __syncthreads();
   if (n > 0) {
 #pragma unroll
     for (int u = 0; u < NS; ++u)
-      if (u * kThreads + tid < n) atomicAdd(&hist[key_of(e[u], E)], 1);
+      if (u * bs + tid < n) atomicAdd(&hist[key_of(e[u], E)], 1);
   }
   __syncthreads();
-  for (int j = tid; j < E; j += kThreads) counts[j] = cap == 0 ? hist[j] : min(hist[j], cap);
+  for (int j = tid; j < E; j += bs) counts[j] = cap == 0 ? hist[j] : min(hist[j], cap);
   if (cap == 0) {  // block-uniform
     block_exclusive_scan(hist, nk, wave_tot);
-    for (int j = tid; j <= E; j += kThreads) offsets[j] = hist[j];
+    for (int j = tid; j <= E; j += bs) offsets[j] = hist[j];
   }
 }
 
 // Per-wave counts for targets k0 .. k0+KC-1 (expert ids te) of the token
-// whose entries start at p0: below[j] = #{entries with code < code_j} and,
-// padded, under[j] = #{entries with code < key_j * n}.  `code` holds this
-// lane's entry codes (INT_MAX past n); the wave's entries are
-// lane + 64*w + 256*u.  Lane 0 of each wave leaves its counts in LDS, and
-// wave 0 the targets' keys.
+// whose entries start at p0, as one unsigned comparison per entry:
+//   packed: c_j = #{entries with lo_j <= code < code_j}, lo_j = 0: the row;
+//   padded: the same with lo_j = key_j * n: the rank among entries with the
+//           same key (codes from key*n up are those of that key or later).
+// (uint)(code - lo) < (uint)(code_j - lo) holds exactly when
+// lo <= code < code_j, because code - lo < 0 wraps to a large value.  `code`
+// holds this lane's entry codes (INT_MAX past n); the wave's entries are
+// lane + 64*w + blockDim*u.  Lane 0 of each wave leaves its counts in LDS,
+// and wave 0 the targets' keys.
 template <int KC, int NS>
 __device__ __forceinline__ void count_targets(const int (&te)[KC], int p0, int k0, int K, int n, int E, bool padded,
-                                              const int (&code)[NS], int nsteps, int* wc_below, int* wc_under,
-                                              int* tkey) {
-  int tk[KC], tcode[KC], tlow[KC];
+                                              const int (&code)[NS], int nsteps, int* wc, int* tkey) {
+  int tk[KC], lo[KC], span[KC], c[KC];
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
     tk[j] = k0 + j < K ? key_of(te[j], E) : E;
-    tcode[j] = tk[j] * n + p0 + k0 + j;
-    tlow[j] = tk[j] * n;
+    lo[j] = padded ? tk[j] * n : 0;
+    span[j] = tk[j] * n + p0 + k0 + j - lo[j];
+    c[j] = 0;
   }
-  int below[KC], under[KC];
-#pragma unroll
-  for (int j = 0; j < KC; ++j) below[j] = under[j] = 0;
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
     if (u >= nsteps) break;  // wave-uniform
 #pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      below[j] += __popcll(wave_ballot(code[u] < tcode[j]));
-      if (padded) under[j] += __popcll(wave_ballot(code[u] < tlow[j]));
-    }
+    for (int j = 0; j < KC; ++j)
+      c[j] += __popcll(wave_ballot(static_cast<uint32_t>(code[u] - lo[j]) < static_cast<uint32_t>(span[j])));
   }
   const int w = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) {
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
       if (k0 + j >= K) break;
-      wc_below[w * kMaxK + k0 + j] = below[j];
-      wc_under[w * kMaxK + k0 + j] = under[j];
+      wc[w * kMaxK + k0 + j] = c[j];
       if (w == 0) tkey[k0 + j] = tk[j];
     }
   }
 }
 
-// NS: 256-entry steps per lane (n <= NS*256).
+// NS: steps of blockDim entries per lane (n <= NS * blockDim).
 template <int KT, bool FP8, int NS>
-__global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(
+__global__ __launch_bounds__(kMaxThreads) void layout_dispatch_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, const float* __restrict__ w, int32_t T,
     int32_t H, int32_t Krt, int32_t E, int32_t cap, uint32_t nchunk, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src, void* __restrict__ recv,
@@ -150,9 +152,9 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(
   const uint32_t b = blockIdx.x - 1;
   const int t = static_cast<int>(b / nchunk);
   const uint32_t chunk = b - static_cast<uint32_t>(t) * nchunk;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int tid = threadIdx.x, bs = blockDim.x, nw = bs / kWave;
   const uint32_t vpt = static_cast<uint32_t>(H) / (FP8 ? 16 : 8);
-  const uint32_t v = chunk * kThreads + tid;  // vector within the token
+  const uint32_t v = chunk * bs + tid;  // vector within the token
   const bool active = v < vpt;
   const int p0 = t * K;
 
@@ -178,43 +180,38 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
-    const int p = u * kThreads + wv * kWave + lane;
+    const int p = u * bs + tid;
     code[u] = p < n ? key_of(code[u], E) * n + p : 0x7FFFFFFF;
   }
 
-  const int nsteps = (n + kThreads - 1) / kThreads;
-  int* wc_below = lds;                   // [kWaves][kMaxK]
-  int* wc_under = lds + kWaves * kMaxK;  // [kWaves][kMaxK]
-  int* rows = lds + 2 * kWaves * kMaxK;  // [kMaxK]
-  int* tkey = rows + kMaxK;              // [kMaxK]
+  const int nsteps = (n + bs - 1) / bs;
+  int* wc = lds;                        // [kMaxWaves][kMaxK]
+  int* rows = lds + kMaxWaves * kMaxK;  // [kMaxK]
+  int* tkey = rows + kMaxK;             // [kMaxK]
   const bool padded = cap > 0;
-  count_targets<KC, NS>(te, p0, 0, K, n, E, padded, code, nsteps, wc_below, wc_under, tkey);
+  count_targets<KC, NS>(te, p0, 0, K, n, E, padded, code, nsteps, wc, tkey);
   for (int k0 = KC; k0 < K; k0 += KC) {  // top-k beyond one pass (generic K only)
 #pragma unroll
     for (int j = 0; j < KC; ++j) te[j] = idx[p0 + min(k0 + j, K - 1)];
-    count_targets<KC, NS>(te, p0, k0, K, n, E, padded, code, nsteps, wc_below, wc_under, tkey);
+    count_targets<KC, NS>(te, p0, k0, K, n, E, padded, code, nsteps, wc, tkey);
   }
   __syncthreads();
 
   // lanes 0..K-1 turn the counts into rows while every lane quantises
   if (tid < K) {
-    int below = 0, under = 0;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      below += wc_below[ww * kMaxK + tid];
-      under += wc_under[ww * kMaxK + tid];
-    }
+    int c = 0;  // packed: the entry's row; padded: its rank within the expert
+    for (int ww = 0; ww < nw; ++ww) c += wc[ww * kMaxK + tid];
     const int k = tkey[tid];
     const bool valid = k < E;
     int row;
     if (!padded) {
-      row = valid ? below : -1;
+      row = valid ? c : -1;
       if (chunk == 0) {
         slot[p0 + tid] = row;
-        src[below] = valid ? t : -1;  // masked entries take the rows after the valid ones
+        src[c] = valid ? t : -1;  // masked entries take the rows after the valid ones
       }
     } else {
-      const int rank = below - under;
+      const int rank = c;
       row = (valid && rank < cap) ? k * cap + rank : -1;
       if (chunk == 0) {
         slot[p0 + tid] = row;
@@ -248,13 +245,29 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(
   }
 }
 
+// Workgroup size.  Up to 2048 entries: 256 lanes, so even 128 tokens fill
+// the chip (FP8 at hidden 7168: two workgroups per token, 257 in all).
+// Beyond, the counting (n*K per workgroup) dominates, and a workgroup
+// takes the whole token (its vectors rounded up to whole waves, at most
+// 1024 lanes) so the ids are read and counted once per token.  Measured on
+// MI355X, top-8, hidden 7168: token-sized workgroups take 7.2 against
+// 6.4 us at 128 tokens, the same 9.0 us at 256, and 11.2 against 12.8 us
+// at 384.
+constexpr int kWideFromEntries = 2048;
+
+int fused_threads(uint32_t vpt, int n) {
+  if (n <= kWideFromEntries) return kMinThreads;
+  const uint32_t lanes = (vpt + kWave - 1) / kWave * kWave;
+  return static_cast<int>(lanes < kMinThreads ? kMinThreads : lanes > kMaxThreads ? kMaxThreads : lanes);
+}
+
 template <bool FP8, int NS>
 void launch_fused(const int32_t* idx, const uint16_t* x, const float* w, int32_t T, int32_t H, int32_t K,
-                  int32_t E, int32_t cap, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
+                  int32_t E, int32_t cap, int bs, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
                   void* recv, float* recv_scale, float* recv_weight, hipStream_t stream) {
   const uint32_t vpt = static_cast<uint32_t>(H) / (FP8 ? 16 : 8);
-  const uint32_t nchunk = (vpt + kThreads - 1) / kThreads;
-  const dim3 grid(1 + static_cast<uint32_t>(T) * nchunk), block(kThreads);
+  const uint32_t nchunk = (vpt + bs - 1) / bs;
+  const dim3 grid(1 + static_cast<uint32_t>(T) * nchunk), block(bs);
 #define EP_FUSED(KV)                                                                                            \
   hipLaunchKernelGGL((layout_dispatch_kernel<KV, FP8, NS>), grid, block, 0, stream, idx, x, w, T, H, K, E, cap, \
                      nchunk, counts, offsets, slot, src, recv, recv_scale, recv_weight)
@@ -273,17 +286,18 @@ template <bool FP8>
 void launch_fused_ns(const int32_t* idx, const uint16_t* x, const float* w, int32_t T, int32_t H, int32_t K,
                      int32_t E, int32_t cap, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
                      void* recv, float* recv_scale, float* recv_weight, hipStream_t stream) {
+  static_assert(kFusedMaxEntries <= 12 * kMinThreads, "steps per lane");
   const int n = T * K;
-  static_assert(kFusedMaxEntries <= 12 * kThreads, "steps per lane");
-  if (n <= 4 * kThreads)
-    launch_fused<FP8, 4>(idx, x, w, T, H, K, E, cap, counts, offsets, slot, src, recv, recv_scale, recv_weight,
+  const int bs = fused_threads(static_cast<uint32_t>(H) / (FP8 ? 16 : 8), n);
+  if (n <= 4 * bs)
+    launch_fused<FP8, 4>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv, recv_scale, recv_weight,
                          stream);
-  else if (n <= 8 * kThreads)
-    launch_fused<FP8, 8>(idx, x, w, T, H, K, E, cap, counts, offsets, slot, src, recv, recv_scale, recv_weight,
+  else if (n <= 8 * bs)
+    launch_fused<FP8, 8>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv, recv_scale, recv_weight,
                          stream);
   else
-    launch_fused<FP8, 12>(idx, x, w, T, H, K, E, cap, counts, offsets, slot, src, recv, recv_scale, recv_weight,
-                          stream);
+    launch_fused<FP8, 12>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv, recv_scale,
+                          recv_weight, stream);
 }
 
 }  // namespace
