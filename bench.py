@@ -409,7 +409,7 @@ def summarize_profile(dirname):
     if dec:
         # steady state: the last 3 of 5 three-call steps (layout, dispatch,
         # combine), then the last 3 of 5 fused steps (layout_dispatch, combine)
-        fwd = ("layout", "dispatch_fp8_kernel", "combine_kernel<8, false>")
+        fwd = ("layout", "dispatch_fp8_kernel", "combine_kernel<8, false,")
         ours = [r for r in dec if short(r["Kernel_Name"]).startswith(fwd)]
         three = ours[:15][-9:]
         fused = ours[15:][-6:]
@@ -447,8 +447,8 @@ def summarize_profile(dirname):
     d_bwd, _ = backward_bytes(T, H, K)
     known = (("layout", alg_bytes(T, H, E, K, True)[0]),
              ("dispatch_fp8_kernel", alg["dispatch_fp8_kernel"]),
-             ("combine_kernel<8, false>", alg["combine_kernel"]),
-             ("combine_kernel<8, true>", d_bwd),  # ep_dispatch_backward
+             ("combine_kernel<8, false,", alg["combine_kernel"]),
+             ("combine_kernel<8, true,", d_bwd),  # ep_dispatch_backward
              ("grad_rows_kernel", 2 * T * H + 8 * T * K + 2 * T * K * H),
              ("grad_weights_kernel", 2 * T * H + 2 * T * K * H + 8 * T * K))
     for prefix, a in known:
@@ -457,9 +457,9 @@ def summarize_profile(dirname):
             if fk is None or wk is None:
                 continue
             fb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
-            lines.append("%-26s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
+            lines.append("%-32s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
                          % (kern, fb, wb, fb + wb, a, (fb + wb) / a))
-            if prefix == "combine_kernel<8, false>":  # the weighted combine
+            if prefix == "combine_kernel<8, false,":  # the weighted combine
                 comb_total = fb + wb
     lines += ["", "combine kernel (the roofline's dominant kernel):",
               "hbm_bytes_per_launch: %.0f" % comb_total,

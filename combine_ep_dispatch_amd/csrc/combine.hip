@@ -13,11 +13,17 @@
 // gfx950 design: bound by HBM reads (K gathered rows per output row).  Work
 // item = (token, 8 channels): the K row indices and weights are loaded
 // first, then all K 16-byte gathers are issued before any arithmetic so that
-// K loads per lane are in flight, then the ordered sum.  The expert rows are
-// read once and the output written once, so both use non-temporal
+// K loads per lane are in flight, then the ordered sum.  Large batches read
+// the expert rows once and write the output once, so both use non-temporal
 // (streaming) accesses: they neither allocate in nor evict from the caches,
 // which on MI355X lifts a gather that otherwise competes with dirty-line
-// write-back from ~3.5-5.0 TB/s to ~5.3-5.7 TB/s.  No LDS, no MFMA.
+// write-back from ~3.5-5.0 TB/s to ~5.3-5.7 TB/s.  Small batches (under
+// 64 MB of gathered rows, e.g. decode: 14.7 MB) use plain accesses, which
+// hit rows still held in the caches (measured 3.1-3.3 against 3.8 us for
+// 128 tokens, top-8, hidden 7168).  No LDS, no MFMA.
+
+// Gathered bytes from which the streaming accesses are used.
+constexpr size_t kStreamingBytes = size_t(64) << 20;
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -28,7 +34,7 @@ namespace {
 constexpr int kThreads = 256;
 
 // Adds the terms of k = k0 .. k0+KC-1 (those < K) to acc, in ascending k.
-template <int KC>
+template <int KC, bool NT>
 __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y, const int32_t* __restrict__ srow,
                                                  const float* __restrict__ wrow, int k0, int K, int32_t H,
                                                  uint32_t v, float (&acc)[8]) {
@@ -44,8 +50,10 @@ __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y,
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
     d[j] = u32x4{0, 0, 0, 0};
-    if (r[j] >= 0)
-      d[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y + static_cast<size_t>(r[j]) * H) + v);
+    if (r[j] >= 0) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(y + static_cast<size_t>(r[j]) * H) + v;
+      d[j] = NT ? __builtin_nontemporal_load(p) : *p;
+    }
   }
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
@@ -59,8 +67,8 @@ __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y,
 }
 
 // UNIT: no weights (every weight 1), the backward of dispatch; a separate
-// instantiation so profiles tell the two uses apart.
-template <int KT, bool UNIT>
+// instantiation so profiles tell the two uses apart.  NT: streaming accesses.
+template <int KT, bool UNIT, bool NT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __restrict__ y,
                                                            const int32_t* __restrict__ slot,
                                                            const float* __restrict__ w, uint32_t n_items,
@@ -78,14 +86,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
   if (KT > 0) {
-    accumulate_chunk<(KT > 0 ? KT : 1)>(y, srow, wrow, 0, K, H, v, acc);
+    accumulate_chunk<(KT > 0 ? KT : 1), NT>(y, srow, wrow, 0, K, H, v, acc);
   } else {
-    for (int k0 = 0; k0 < K; k0 += 8) accumulate_chunk<8>(y, srow, wrow, k0, K, H, v, acc);
+    for (int k0 = 0; k0 < K; k0 += 8) accumulate_chunk<8, NT>(y, srow, wrow, k0, K, H, v, acc);
   }
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
-  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + static_cast<size_t>(t) * H) + v);
+  u32x4* dst = reinterpret_cast<u32x4*>(out + static_cast<size_t>(t) * H) + v;
+  if (NT)
+    __builtin_nontemporal_store(o, dst);
+  else
+    *dst = o;
 }
 
 }  // namespace
@@ -96,11 +108,15 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w
   const uint32_t n_items = static_cast<uint32_t>(T) * vpt;
   if (n_items == 0) return hipSuccess;
   const dim3 grid((n_items + kThreads - 1) / kThreads), block(kThreads);
-#define EP_COMBINE(KV)                                                                                 \
-  if (w == nullptr)                                                                                    \
-    hipLaunchKernelGGL((combine_kernel<KV, true>), grid, block, 0, stream, y, slot, w, n_items, vpt, H, K, out); \
-  else                                                                                                 \
-    hipLaunchKernelGGL((combine_kernel<KV, false>), grid, block, 0, stream, y, slot, w, n_items, vpt, H, K, out)
+  const bool nt = static_cast<size_t>(T) * K * H * 2 >= kStreamingBytes;
+#define EP_COMBINE_NT(KV, U, NTV) \
+  hipLaunchKernelGGL((combine_kernel<KV, U, NTV>), grid, block, 0, stream, y, slot, w, n_items, vpt, H, K, out)
+#define EP_COMBINE(KV)                                                     \
+  if (w == nullptr) {                                                      \
+    if (nt) EP_COMBINE_NT(KV, true, true); else EP_COMBINE_NT(KV, true, false);   \
+  } else {                                                                 \
+    if (nt) EP_COMBINE_NT(KV, false, true); else EP_COMBINE_NT(KV, false, false); \
+  }
   switch (K) {
     case 1: { EP_COMBINE(1); } break;
     case 2: { EP_COMBINE(2); } break;
@@ -110,6 +126,7 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w
     default: { EP_COMBINE(0); } break;
   }
 #undef EP_COMBINE
+#undef EP_COMBINE_NT
   return hipGetLastError();
 }
 

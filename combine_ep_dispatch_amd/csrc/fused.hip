@@ -159,7 +159,9 @@ __global__ __launch_bounds__(kMaxThreads) void layout_dispatch_kernel(
   const int p0 = t * K;
 
   // every load up front: the token's expert ids, the token itself (its
-  // latency overlaps the counting), then all ids
+  // latency overlaps the counting), then all ids.  The token is read with
+  // plain loads: at these sizes it is usually still in the caches (measured
+  // 5.7 against 6.0 us with streaming loads at 128 tokens)
   int te[KC];
 #pragma unroll
   for (int j = 0; j < KC; ++j) te[j] = idx[p0 + min(j, K - 1)];
@@ -167,10 +169,10 @@ __global__ __launch_bounds__(kMaxThreads) void layout_dispatch_kernel(
   if (active) {
     const u32x4* px = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * H);
     if (FP8) {
-      a = __builtin_nontemporal_load(px + 2 * v);
-      a2 = __builtin_nontemporal_load(px + 2 * v + 1);
+      a = px[2 * v];
+      a2 = px[2 * v + 1];
     } else {
-      a = __builtin_nontemporal_load(px + v);
+      a = px[v];
     }
   }
   int code[NS];
