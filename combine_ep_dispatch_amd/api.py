@@ -11,6 +11,7 @@ and a handle, and ``combine(...)`` reducing back ([P4] "使用示例 › MoE 训
 的应用"; [P5] "典型工作流程").
 """
 
+import os
 from collections import namedtuple
 
 import torch
@@ -28,6 +29,21 @@ def _stream(stream):
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+# EP_DEBUG_CHECK=1: reject expert ids outside [-1, E) before launching.  The
+# kernels mask every id outside [0, E), so such ids are legal; an id other
+# than -1 out there is usually a caller bug.  The check reads the ids'
+# range back to the host (a synchronisation), so it is off by default.
+DEBUG_CHECK = os.environ.get("EP_DEBUG_CHECK") == "1"
+
+
+def _debug_check_ids(topk_idx, num_experts):
+    if not DEBUG_CHECK or topk_idx.numel() == 0:
+        return
+    lo, hi = int(topk_idx.min()), int(topk_idx.max())
+    if lo < -1 or hi >= num_experts:
+        raise ValueError("EP_DEBUG_CHECK: topk_idx holds ids in [%d, %d], outside [-1, %d)" % (lo, hi, num_experts))
 
 
 def _need(t, name, dtypes, shape=None):
@@ -56,6 +72,7 @@ def ep_layout_workspace_bytes(num_tokens, top_k, num_experts):
 def ep_dispatch_layout(topk_idx, num_experts, tokens_per_expert, expert_offset, slot, src_token,
                        workspace=None, stream=None):
     _need(topk_idx, "topk_idx", _I32)
+    _debug_check_ids(topk_idx, num_experts)
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [T, K]")
     T, K = topk_idx.shape
@@ -76,6 +93,7 @@ def ep_dispatch_layout(topk_idx, num_experts, tokens_per_expert, expert_offset, 
 def ep_dispatch_layout_padded(topk_idx, num_experts, capacity, recv_expert_count, slot, src_token,
                               workspace=None, stream=None):
     _need(topk_idx, "topk_idx", _I32)
+    _debug_check_ids(topk_idx, num_experts)
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [T, K]")
     T, K = topk_idx.shape
@@ -133,6 +151,7 @@ def ep_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format,
     receive rows); capacity > 0: padded layout (expert_offset None,
     src_token [E*capacity], E*capacity receive rows)."""
     _need(topk_idx, "topk_idx", _I32)
+    _debug_check_ids(topk_idx, num_experts)
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [T, K]")
     T, K = topk_idx.shape

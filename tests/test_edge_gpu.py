@@ -174,3 +174,22 @@ def test_layout_unaligned_ids(gpu, rows):
     oc, oo, os_, osrc = oracle.dispatch_layout(idx, 256)
     assert np.array_equal(host(counts), oc) and np.array_equal(host(offsets), oo)
     assert np.array_equal(host(slot), os_) and np.array_equal(host(src), osrc)
+
+
+def test_debug_check_rejects_ids_outside_minus_one_to_e(gpu, monkeypatch):
+    """With EP_DEBUG_CHECK on, the binding refuses ids outside [-1, E)
+    before any launch; -1 (masked) passes, and with the check off the same
+    ids are masked by the kernels."""
+    import combine_ep_dispatch_amd.api as api
+    ep = gpu
+    E = 16
+    idx = np.array([[0, 5], [-1, 15], [3, 16]], dtype=np.int32)
+    print("case debug check", flush=True)
+    monkeypatch.setattr(api, "DEBUG_CHECK", True)
+    with pytest.raises(ValueError, match="EP_DEBUG_CHECK"):
+        gpu_layout(ep, idx, E)
+    counts, offsets, slot, src = gpu_layout(ep, idx[:2], E)  # only -1 out of range: accepted
+    assert np.array_equal(host(slot), oracle.dispatch_layout(idx[:2], E)[2])
+    monkeypatch.setattr(api, "DEBUG_CHECK", False)
+    counts, offsets, slot, src = gpu_layout(ep, idx, E)  # 16 is masked
+    assert np.array_equal(host(slot), oracle.dispatch_layout(idx, E)[2])

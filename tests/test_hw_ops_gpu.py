@@ -43,6 +43,31 @@ def test_cast_sweep_rounding_band(gpu):
     assert np.array_equal(host(out), oracle.f32_to_e4m3_rne_sat(v))
 
 
+def test_cast_tails_exhaustive(gpu):
+    """Every finite binary32 outside the band above, both signs: below 2^-12
+    the code is a signed zero, from 2^10 up it saturates to +-448 (0x7E).
+    The oracle's encoder gives exactly these codes on the sampled tails of
+    the previous test; here all ~3.9e9 inputs are generated and compared on
+    the device, in chunks.  With the band above this covers every finite
+    binary32 (NaN and infinity are outside the contract)."""
+    ep = gpu
+    band_lo, band_hi, inf_bits = (127 - 12) << 23, (127 + 10) << 23, 0x7F800000
+    chunk = 1 << 28
+    for start, stop, code in ((0, band_lo, 0x00), (band_hi, inf_bits, 0x7E)):
+        for a in range(start, stop, chunk):
+            b = min(stop, a + chunk)
+            bits = torch.arange(a, b, dtype=torch.int64, device="cuda").to(torch.int32)
+            for sign in (0, 1):
+                v = (bits | torch.tensor(-(2 ** 31), dtype=torch.int32, device="cuda")) if sign else bits
+                out = torch.empty(b - a, dtype=torch.uint8, device="cuda")
+                ep.ep_cast_fp8_e4m3(v.view(torch.float32), out)
+                want = code | (sign << 7)
+                bad = torch.nonzero(out != want)
+                assert bad.numel() == 0, (hex(a), sign, hex(int(bits[bad[0, 0]])), int(out[bad[0, 0]]), hex(want))
+            del bits, v, out
+    torch.cuda.synchronize()
+
+
 def division_sensitive_groups(n_groups=512, seed=4):
     """Groups whose quotients x/s sit on or next to E4M3 midpoints, where a
     reciprocal-multiply or a wrongly rounded division flips the code."""

@@ -46,6 +46,22 @@ def test_e4m3_saturation_and_ties():
     assert enc1(np.nextafter(np.float32(2.0 ** -10), np.float32(1))) == 0x01
 
 
+def test_e4m3_tails_are_constant():
+    """Outside [2**-12, 2**10) the code depends only on the sign: below 2**-12
+    a value is under half the smallest subnormal (2**-10), so it rounds to
+    a signed zero; from 2**10 up it is beyond 448, so it saturates.  Random
+    bit patterns from both tails (the GPU test sweeps them all on the
+    device against exactly these constants)."""
+    rng = np.random.default_rng(3)
+    lo = rng.integers(0, (127 - 12) << 23, 200_000, dtype=np.uint64).astype(np.uint32)
+    hi = rng.integers((127 + 10) << 23, 0x7F800000, 200_000, dtype=np.uint64).astype(np.uint32)
+    sign = np.uint32(0x80000000)
+    assert np.all(f32_to_e4m3_rne_sat(lo.view(np.float32)) == 0x00)
+    assert np.all(f32_to_e4m3_rne_sat((lo | sign).view(np.float32)) == 0x80)
+    assert np.all(f32_to_e4m3_rne_sat(hi.view(np.float32)) == 0x7E)
+    assert np.all(f32_to_e4m3_rne_sat((hi | sign).view(np.float32)) == 0xFE)
+
+
 def test_e4m3_decode_all_codes():
     codes = np.arange(256, dtype=np.uint8)
     dec = e4m3_to_f32(codes)
