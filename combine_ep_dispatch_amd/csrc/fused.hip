@@ -34,9 +34,9 @@
 // workgroup writes its part of the K receive rows.  Every workgroup reads
 // all n ids (4n bytes, from L2 after the first) and compares them with its
 // token's K codes, so the counting grows as n*K per workgroup.  On MI355X
-// (256 experts, top-8, hidden 7168) one launch takes 6.4 us against 4.0 +
-// 4.9 us for the two kernels at 1024 entries, 8.6 against 11.4 us at 2048
-// and 10.9 against 12.6 us at 3072, and breaks even at 4096; the path is
+// (256 experts, top-8, hidden 7168) one launch takes 6.3 us against 4.0 +
+// 4.8 us for the two kernels at 1024 entries, 8.3 against 11.5 us at 2048
+// and 10.1 against 12.4 us at 3072, and breaks even at 4096; the path is
 // used up to 3072 entries, and larger batches run the layout kernels and
 // the dispatch kernel.
 
@@ -134,9 +134,11 @@ __device__ __forceinline__ void count_targets(const int (&te)[KC], int p0, int k
   }
 }
 
-// NS: steps of blockDim entries per lane (n <= NS * blockDim).
-template <int KT, bool FP8, int NS>
-__global__ __launch_bounds__(kMaxThreads) void layout_dispatch_kernel(
+// NS: steps of blockDim entries per lane (n <= NS * blockDim).  MAXT: the
+// largest workgroup the instantiation is launched with (256, or 1024 for
+// token-wide workgroups); the tighter bound measured 0.25-0.45 us faster.
+template <int KT, bool FP8, int NS, int MAXT>
+__global__ __launch_bounds__(MAXT) void layout_dispatch_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, const float* __restrict__ w, int32_t T,
     int32_t H, int32_t Krt, int32_t E, int32_t cap, uint32_t nchunk, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src, void* __restrict__ recv,
@@ -263,7 +265,7 @@ int fused_threads(uint32_t vpt, int n) {
   return static_cast<int>(lanes < kMinThreads ? kMinThreads : lanes > kMaxThreads ? kMaxThreads : lanes);
 }
 
-template <bool FP8, int NS>
+template <bool FP8, int NS, int MAXT>
 void launch_fused(const int32_t* idx, const uint16_t* x, const float* w, int32_t T, int32_t H, int32_t K,
                   int32_t E, int32_t cap, int bs, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
                   void* recv, float* recv_scale, float* recv_weight, hipStream_t stream) {
@@ -271,7 +273,7 @@ void launch_fused(const int32_t* idx, const uint16_t* x, const float* w, int32_t
   const uint32_t nchunk = (vpt + bs - 1) / bs;
   const dim3 grid(1 + static_cast<uint32_t>(T) * nchunk), block(bs);
 #define EP_FUSED(KV)                                                                                            \
-  hipLaunchKernelGGL((layout_dispatch_kernel<KV, FP8, NS>), grid, block, 0, stream, idx, x, w, T, H, K, E, cap, \
+  hipLaunchKernelGGL((layout_dispatch_kernel<KV, FP8, NS, MAXT>), grid, block, 0, stream, idx, x, w, T, H, K, E, cap, \
                      nchunk, counts, offsets, slot, src, recv, recv_scale, recv_weight)
   switch (K) {
     case 1: EP_FUSED(1); break;
@@ -291,15 +293,28 @@ void launch_fused_ns(const int32_t* idx, const uint16_t* x, const float* w, int3
   static_assert(kFusedMaxEntries <= 12 * kMinThreads, "steps per lane");
   const int n = T * K;
   const int bs = fused_threads(static_cast<uint32_t>(H) / (FP8 ? 16 : 8), n);
-  if (n <= 4 * bs)
-    launch_fused<FP8, 4>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv, recv_scale, recv_weight,
-                         stream);
-  else if (n <= 8 * bs)
-    launch_fused<FP8, 8>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv, recv_scale, recv_weight,
-                         stream);
-  else
-    launch_fused<FP8, 12>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv, recv_scale,
-                          recv_weight, stream);
+  // steps per lane: n <= 3072 and bs >= 256, so at most 12
+  const int steps = (n + bs - 1) / bs;
+  if (bs == kMinThreads) {
+    if (steps <= 4)
+      launch_fused<FP8, 4, kMinThreads>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv, recv_scale,
+                                        recv_weight, stream);
+    else if (steps <= 8)
+      launch_fused<FP8, 8, kMinThreads>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv, recv_scale,
+                                        recv_weight, stream);
+    else
+      launch_fused<FP8, 12, kMinThreads>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv,
+                                         recv_scale, recv_weight, stream);
+  } else if (steps <= 4) {
+    launch_fused<FP8, 4, kMaxThreads>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv, recv_scale,
+                                      recv_weight, stream);
+  } else if (steps <= 8) {
+    launch_fused<FP8, 8, kMaxThreads>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv, recv_scale,
+                                      recv_weight, stream);
+  } else {
+    launch_fused<FP8, 12, kMaxThreads>(idx, x, w, T, H, K, E, cap, bs, counts, offsets, slot, src, recv,
+                                       recv_scale, recv_weight, stream);
+  }
 }
 
 }  // namespace
