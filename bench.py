@@ -589,6 +589,9 @@ def main():
         "step_distribution_us": dict(dist, note="50 steps each timed alone (events between the calls); flushed: "
                                                 "a 512 MB device read before every step evicts the Infinity Cache"),
         "flushed_GBs_at_median": round(total_b / dist["flushed"]["step"]["median"] / 1e3, 1),
+        "decode_us_per_step": decode[0]["fused"]["stream_step_plan"],
+        "decode_step": "128 tokens x 7168, 256 experts, top-8, FP8: ep_layout_dispatch + ep_combine through "
+                       "StepPlan, eager, mean of 200 back-to-back steps (HIP events on the launch stream)",
         "decode_128tok_us": dict(decode[0], low_latency_padded_128=decode[128]),
         "backward_us": {"dispatch_backward": round(db_us, 2), "combine_backward": round(cb_us, 2),
                         "dispatch_backward_GBs": round(db_b / db_us / 1e3, 1),
