@@ -37,8 +37,13 @@ sys.path.insert(0, ROOT)
 METRIC = "dispatch+combine µs and achieved HBM GB/s at 4096x7168 top-8; µs at 128 tok"
 PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E peak
 PROFILES = os.path.join(ROOT, "profiles")
-COMBINE_SOURCES = ["combine_ep_dispatch_amd/csrc/combine.hip", "combine_ep_dispatch_amd/csrc/ep_device.h"]
-TRAFFIC_FILE = os.path.join(PROFILES, "combine_prefill_4096x7168_top8_traffic.txt")
+# every kernel source: counter bytes are reported only while these are unchanged
+KERNEL_SOURCES = sorted("combine_ep_dispatch_amd/csrc/" + f for f in os.listdir(os.path.join(ROOT, "combine_ep_dispatch_amd", "csrc"))
+                        if f.endswith((".hip", ".h")))
+TRAFFIC_FILE = os.path.join(PROFILES, "prefill_4096x7168_top8_counter_traffic.txt")
+# the prefill step's kernels as they appear in the profile
+STEP_KERNELS = {"layout": "layout_fused<16, true>", "dispatch": "dispatch_fp8_kernel<8>",
+                "combine": "combine_kernel<8, false, true>"}
 
 
 def backward_bytes(T, H, K):
@@ -283,8 +288,9 @@ def time_calls(torch, fn, reps, warmup=3):
 
 
 def read_traffic():
-    """HBM bytes per combine launch from the committed rocprofv3 counter
-    summary, or None when the kernel source changed since it was taken."""
+    """HBM bytes per launch of the step's kernels ({"layout", "dispatch",
+    "combine"}) from the committed rocprofv3 counter summary, or None when
+    any kernel source changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -292,10 +298,10 @@ def read_traffic():
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_sha256") != source_hash(COMBINE_SOURCES):
+    if vals.get("source_sha256") != source_hash(KERNEL_SOURCES):
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return {step: float(vals["hbm_bytes_per_launch[%s]" % step]) for step in STEP_KERNELS}
     except (KeyError, ValueError):
         return None
 
@@ -443,7 +449,6 @@ def summarize_profile(dirname):
              "WRITE_SIZE %.1f KiB" % (avg[("__amd_rocclr_copyBuffer", "FETCH_SIZE")],
                                       avg[("__amd_rocclr_copyBuffer", "WRITE_SIZE")]),
              "fetch_scale: %.4f" % f_fetch, "write_scale: %.4f" % f_write, ""]
-    comb_total = None
     d_bwd, _ = backward_bytes(T, H, K)
     known = (("layout", alg_bytes(T, H, E, K, True)[0]),
              ("dispatch_fp8_kernel", alg["dispatch_fp8_kernel"]),
@@ -459,12 +464,16 @@ def summarize_profile(dirname):
             fb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
             lines.append("%-32s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
                          % (kern, fb, wb, fb + wb, a, (fb + wb) / a))
-            if prefix == "combine_kernel<8, false,":  # the weighted combine
-                comb_total = fb + wb
-    lines += ["", "combine kernel (the roofline's dominant kernel):",
-              "hbm_bytes_per_launch: %.0f" % comb_total,
-              "source_sha256: %s" % source_hash(COMBINE_SOURCES),
-              "(sha256 prefix of %s; bench.py reports traffic only while it matches)" % ", ".join(COMBINE_SOURCES)]
+    totals = {}
+    for kern in {k for (k, c) in avg}:
+        fk, wk = avg.get((kern, "FETCH_SIZE")), avg.get((kern, "WRITE_SIZE"))
+        if fk is not None and wk is not None:
+            totals[kern] = fk * 1024 * f_fetch + wk * 1024 * f_write
+    lines += ["", "the prefill step's kernels (combine is the roofline's dominant kernel):"]
+    lines += ["hbm_bytes_per_launch[%s]: %.0f" % (step, totals[kern]) for step, kern in STEP_KERNELS.items()]
+    lines += ["source_sha256: %s" % source_hash(KERNEL_SOURCES),
+              "(sha256 prefix of every file under combine_ep_dispatch_amd/csrc; bench.py reports counter bytes "
+              "only while it matches)"]
     with open(TRAFFIC_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
     for p in ("prefill_4096x7168_top8_kernel_trace.txt", "decode_128x7168_top8_kernel_trace.txt",
@@ -598,11 +607,14 @@ def main():
                         "combine_backward_GBs": round(cb_b / cb_us / 1e3, 1)},
         "roofline": {"bound": "hbm", "kernel": "combine", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic["combine"] if traffic else None},
     }
     if traffic is not None:
-        # the same launch duration over the bytes the HBM counters saw
-        rec["roofline"]["traffic_GBs"] = round(traffic / (comb_us * 1e-6) / 1e9, 1)
+        # each kernel's mean launch duration over the bytes the HBM counters saw
+        rec["roofline"]["traffic_GBs"] = round(traffic["combine"] / (comb_us * 1e-6) / 1e9, 1)
+        rec["counter_bytes_per_launch"] = {k: int(v) for k, v in traffic.items()}
+        rec["counter_GBs"] = {k: round(traffic[k] / (per_kernel[k] * 1e-6) / 1e9, 1) for k in traffic}
+        rec["counter_GBs_step"] = round(sum(traffic.values()) / (us_step * 1e-6) / 1e9, 1)
     rec["context_pages"] = {
         "note": "DeepEP on H800, multi-GPU all-to-all over interconnects; context, not a target",
         "normal_kernels_nvlink_GBs": "153-158", "normal_kernels_rdma_GBs": "43-47",
