@@ -499,6 +499,10 @@ def other_workload(ep, torch, args):
            "kernel_GBs": {"dispatch": round(dis_b / per_kernel["dispatch"] / 1e3, 1),
                           "combine": round(com_b / per_kernel["combine"] / 1e3, 1)},
            "kernel_alg_bytes": {"layout": lay_b, "dispatch": dis_b, "combine": com_b}}
+    if wl.T * wl.K <= 3072:
+        # small batches: the one-launch layout + dispatch through StepPlan
+        plan = ep.StepPlan(s.idx, s.w, s.x, wl.E, fp8=wl.fp8, y=s.y)
+        rec["us_per_step_fused_step_plan"] = round(time_loop(torch, plan.step, args.steps, args.warmup), 2)
     print(json.dumps(rec), flush=True)
     return 0
 
