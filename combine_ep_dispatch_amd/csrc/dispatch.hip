@@ -15,7 +15,9 @@
 // one 128-channel group, so the group max is three DPP steps inside the
 // wavefront; the division is IEEE correctly rounded (no reciprocal
 // shortcut), and the conversion is gfx950's OCP FP8 convert.  The token is
-// read once, with non-temporal loads; the receive rows are written with
+// read once, with non-temporal loads (about 10% faster at 4096 tokens), or
+// with plain loads when the batch is small enough to be cache-resident
+// (under 16 MB of tokens, e.g. decode); the receive rows are written with
 // plain stores, which on MI355X sustain ~6.3 TB/s where non-temporal ones
 // reach ~4.8 TB/s (and far less for these scattered 1 KB row segments).
 // Not ALU-bound: replacing the division by a reciprocal multiply is not
@@ -28,6 +30,12 @@ namespace ep {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr size_t kStreamingTokenBytes = size_t(16) << 20;  // from here on, non-temporal token loads
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load_token(const u32x4* p) {
+  return NT ? __builtin_nontemporal_load(p) : *p;
+}
 
 // Receive rows (and weights) of entries k0 .. k0+KC-1 of one token, loaded
 // together before any store so their latencies overlap.
@@ -42,7 +50,7 @@ __device__ __forceinline__ void load_rows(const int32_t* __restrict__ srow, cons
   }
 }
 
-template <int KT>
+template <int KT, bool NT>
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const uint16_t* __restrict__ x, uint32_t n_items, uint32_t vpt, int32_t H, int32_t Krt,
     const int32_t* __restrict__ slot, const float* __restrict__ w, uint8_t* __restrict__ recv,
@@ -66,8 +74,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
   u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
   if (active) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * H) + 2 * v;
-    a = __builtin_nontemporal_load(src);
-    b = __builtin_nontemporal_load(src + 1);
+    a = load_token<NT>(src);
+    b = load_token<NT>(src + 1);
   }
   float s;
   const u32x4 q = quantize16_e4m3(a, b, s);
@@ -89,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
   }
 }
 
-template <int KT>
+template <int KT, bool NT>
 __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const uint16_t* __restrict__ x, uint32_t n_items, uint32_t vpt, int32_t H, int32_t Krt,
     const int32_t* __restrict__ slot, const float* __restrict__ w, uint16_t* __restrict__ recv,
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
   int32_t r[KC];
   float wk[KC];
   load_rows<KC>(srow, wrow, 0, K, want_w, r, wk);
-  const u32x4 d = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * H) + v);
+  const u32x4 d = load_token<NT>(reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * H) + v);
   for (int k0 = 0;;) {
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
@@ -143,16 +151,21 @@ hipError_t launch_dispatch_fp8(const uint16_t* x, int32_t T, int32_t H, int32_t 
   const uint32_t n_items = static_cast<uint32_t>(T) * vpt;
   if (n_items == 0) return hipSuccess;
   const dim3 grid((n_items + kThreads - 1) / kThreads), block(kThreads);
-#define EP_DISPATCH_FP8(KV)                                                                        \
-  hipLaunchKernelGGL(dispatch_fp8_kernel<KV>, grid, block, 0, stream, x, n_items, vpt, H, K, slot, w, \
-                     recv, recv_scale, recv_weight)
+  const bool nt = static_cast<size_t>(T) * H * 2 >= kStreamingTokenBytes;
+#define EP_DISPATCH_FP8(KV)                                                                                 \
+  if (nt)                                                                                                   \
+    hipLaunchKernelGGL((dispatch_fp8_kernel<KV, true>), grid, block, 0, stream, x, n_items, vpt, H, K, slot, w, \
+                       recv, recv_scale, recv_weight);                                                      \
+  else                                                                                                      \
+    hipLaunchKernelGGL((dispatch_fp8_kernel<KV, false>), grid, block, 0, stream, x, n_items, vpt, H, K, slot, w, \
+                       recv, recv_scale, recv_weight)
   switch (K) {
-    case 1: EP_DISPATCH_FP8(1); break;
-    case 2: EP_DISPATCH_FP8(2); break;
-    case 4: EP_DISPATCH_FP8(4); break;
-    case 6: EP_DISPATCH_FP8(6); break;
-    case 8: EP_DISPATCH_FP8(8); break;
-    default: EP_DISPATCH_FP8(0); break;
+    case 1: { EP_DISPATCH_FP8(1); } break;
+    case 2: { EP_DISPATCH_FP8(2); } break;
+    case 4: { EP_DISPATCH_FP8(4); } break;
+    case 6: { EP_DISPATCH_FP8(6); } break;
+    case 8: { EP_DISPATCH_FP8(8); } break;
+    default: { EP_DISPATCH_FP8(0); } break;
   }
 #undef EP_DISPATCH_FP8
   return hipGetLastError();
@@ -164,16 +177,21 @@ hipError_t launch_dispatch_bf16(const uint16_t* x, int32_t T, int32_t H, int32_t
   const uint32_t n_items = static_cast<uint32_t>(T) * vpt;
   if (n_items == 0) return hipSuccess;
   const dim3 grid((n_items + kThreads - 1) / kThreads), block(kThreads);
-#define EP_DISPATCH_BF16(KV)                                                                        \
-  hipLaunchKernelGGL(dispatch_bf16_kernel<KV>, grid, block, 0, stream, x, n_items, vpt, H, K, slot, w, \
-                     recv, recv_weight)
+  const bool nt = static_cast<size_t>(T) * H * 2 >= kStreamingTokenBytes;
+#define EP_DISPATCH_BF16(KV)                                                                                 \
+  if (nt)                                                                                                    \
+    hipLaunchKernelGGL((dispatch_bf16_kernel<KV, true>), grid, block, 0, stream, x, n_items, vpt, H, K, slot, w, \
+                       recv, recv_weight);                                                                   \
+  else                                                                                                       \
+    hipLaunchKernelGGL((dispatch_bf16_kernel<KV, false>), grid, block, 0, stream, x, n_items, vpt, H, K, slot, w, \
+                       recv, recv_weight)
   switch (K) {
-    case 1: EP_DISPATCH_BF16(1); break;
-    case 2: EP_DISPATCH_BF16(2); break;
-    case 4: EP_DISPATCH_BF16(4); break;
-    case 6: EP_DISPATCH_BF16(6); break;
-    case 8: EP_DISPATCH_BF16(8); break;
-    default: EP_DISPATCH_BF16(0); break;
+    case 1: { EP_DISPATCH_BF16(1); } break;
+    case 2: { EP_DISPATCH_BF16(2); } break;
+    case 4: { EP_DISPATCH_BF16(4); } break;
+    case 6: { EP_DISPATCH_BF16(6); } break;
+    case 8: { EP_DISPATCH_BF16(8); } break;
+    default: { EP_DISPATCH_BF16(0); } break;
   }
 #undef EP_DISPATCH_BF16
   return hipGetLastError();
