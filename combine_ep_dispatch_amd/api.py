@@ -51,11 +51,11 @@ def _need(t, name, dtypes, shape=None):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.dtype not in dtypes:
         raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
-    if t.device.type != "cuda":
+    if not t.is_cuda:  # (a ROCm device tensor reports is_cuda; cheaper than t.device.type)
         raise ValueError("%s must be on a GPU device" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != tuple(shape):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
 
