@@ -23,7 +23,11 @@ class StepPlan:
     expert of the low-latency layout (E*capacity rows); fp8 selects the
     receive format.  y (expert outputs, bf16 [rows, H]) defaults to a new
     tensor; all other buffers are allocated here.  The stream is fixed at
-    construction (the current stream by default).
+    construction (the current stream by default).  To replay a step as a
+    HIP graph, build the plan on a side stream and capture on it:
+    ``torch.cuda.graph(g, stream=that_stream)``; the plan's input tensors
+    can be refilled between replays.  The library keeps no state, so plans
+    on different streams may run at the same time.
     """
 
     def __init__(self, topk_idx, topk_weights, x, num_experts, capacity=0, fp8=True, y=None, stream=None):

@@ -57,3 +57,79 @@ def test_step_plan_matches_oracle(gpu, name, T, capacity, fp8, separate):
         orecv = oracle.dispatch_bf16(wl.x_bits, oslot, num_rows=rows)
         assert np.array_equal(host(plan.recv_x.view(torch.int16))[valid], orecv[valid])
     assert np.array_equal(host(plan.out.view(torch.int16)), oracle.combine(y, oslot, wl.topk_weights))
+
+
+@pytest.mark.parametrize("capacity", [0, 128])
+def test_step_plan_in_a_graph(gpu, capacity):
+    """A plan built on a side stream and captured there: every replay, with
+    new routing and tokens copied into the plan's inputs in between, equals
+    the oracle for those inputs."""
+    ep = gpu
+    side = torch.cuda.Stream()
+    wl = make_workload("decode", seed=21)
+    idx = torch.from_numpy(wl.topk_idx).cuda()
+    w = torch.from_numpy(wl.topk_weights).cuda()
+    x = torch.from_numpy(wl.x_bits.view(np.int16)).cuda()
+    print("case plan graph", capacity, flush=True)
+    plan = ep.StepPlan(idx, w, x, wl.E, capacity=capacity, stream=side)
+    rng = np.random.default_rng(21)
+    y = to_bf16_bits(rng.standard_normal((plan.rows, wl.H), dtype=np.float32))
+    plan.y.copy_(torch.from_numpy(y.view(np.int16)).cuda().view(torch.bfloat16))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        plan.step()  # warm up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        plan.step()
+    for seed in (22, 23, 24):
+        wl2 = make_workload("decode", seed=seed)
+        idx.copy_(torch.from_numpy(wl2.topk_idx))
+        w.copy_(torch.from_numpy(wl2.topk_weights))
+        x.copy_(torch.from_numpy(wl2.x_bits.view(np.int16)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if capacity:
+            oc, oslot, _ = oracle.dispatch_layout_padded(wl2.topk_idx, wl2.E, capacity)
+            valid = (np.arange(capacity)[None, :] < oc[:, None]).ravel()
+        else:
+            oc, oo, oslot, _ = oracle.dispatch_layout(wl2.topk_idx, wl2.E)
+            valid = np.arange(plan.rows) < oo[-1]
+        assert np.array_equal(host(plan.counts), oc) and np.array_equal(host(plan.slot), oslot)
+        orecv, oscale, _ = oracle.dispatch_fp8(wl2.x_bits, oslot, num_rows=plan.rows)
+        assert np.array_equal(host(plan.recv_x)[valid], orecv[valid])
+        assert np.array_equal(host(plan.recv_scale)[valid].view(np.uint32), oscale[valid].view(np.uint32))
+        assert np.array_equal(host(plan.out.view(torch.int16)), oracle.combine(y, oslot, wl2.topk_weights))
+
+
+def test_two_streams_at_once(gpu):
+    """The library keeps no state: two plans stepping on two streams at the
+    same time each produce their own oracle result."""
+    ep = gpu
+    plans, ys, wls = [], [], []
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    print("case two streams", flush=True)
+    for i, s in enumerate(streams):
+        wl = make_workload("decode", seed=30 + i)
+        idx = torch.from_numpy(wl.topk_idx).cuda()
+        w = torch.from_numpy(wl.topk_weights).cuda()
+        x = torch.from_numpy(wl.x_bits.view(np.int16)).cuda()
+        plan = ep.StepPlan(idx, w, x, wl.E, stream=s)
+        y = to_bf16_bits(np.random.default_rng(30 + i).standard_normal((plan.rows, wl.H), dtype=np.float32))
+        plan.y.copy_(torch.from_numpy(y.view(np.int16)).cuda().view(torch.bfloat16))
+        plans.append(plan)
+        ys.append(y)
+        wls.append(wl)
+    torch.cuda.synchronize()
+    for _ in range(20):  # interleaved launches on the two streams
+        for plan in plans:
+            plan.step()
+    torch.cuda.synchronize()
+    for plan, y, wl in zip(plans, ys, wls):
+        oc, oo, oslot, osrc = oracle.dispatch_layout(wl.topk_idx, wl.E)
+        assert np.array_equal(host(plan.slot), oslot) and np.array_equal(host(plan.src), osrc)
+        nv = int(oo[-1])
+        orecv, oscale, _ = oracle.dispatch_fp8(wl.x_bits, oslot)
+        assert np.array_equal(host(plan.recv_x)[:nv], orecv[:nv])
+        assert np.array_equal(host(plan.out.view(torch.int16)), oracle.combine(y, oslot, wl.topk_weights))
