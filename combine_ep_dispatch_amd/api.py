@@ -66,11 +66,19 @@ _U8 = (torch.uint8, torch.float8_e4m3fn)
 
 
 def ep_layout_workspace_bytes(num_tokens, top_k, num_experts):
+    """Bytes of device workspace the layout calls need for this shape (0 up
+    to 65536 entries, T*K)."""
     return int(LIB.ep_layout_workspace_bytes(int(num_tokens), int(top_k), int(num_experts)))
 
 
 def ep_dispatch_layout(topk_idx, num_experts, tokens_per_expert, expert_offset, slot, src_token,
                        workspace=None, stream=None):
+    """Routing layout into caller-owned int32 tensors: tokens_per_expert [E],
+    expert_offset [E+1] (exclusive scan), slot [T, K] (receive row of entry
+    (t, k), -1 if masked), src_token [T*K] (token of each row, -1 past
+    expert_offset[E]).  Rows of one expert are in ascending token order.
+    workspace: uint8/int32 device tensor of ep_layout_workspace_bytes bytes
+    (only needed past 65536 entries)."""
     _need(topk_idx, "topk_idx", _I32)
     _debug_check_ids(topk_idx, num_experts)
     if topk_idx.dim() != 2:
@@ -92,6 +100,10 @@ def ep_dispatch_layout(topk_idx, num_experts, tokens_per_expert, expert_offset, 
 
 def ep_dispatch_layout_padded(topk_idx, num_experts, capacity, recv_expert_count, slot, src_token,
                               workspace=None, stream=None):
+    """Low-latency layout: expert e owns rows e*capacity .. e*capacity +
+    capacity - 1; recv_expert_count [E] = min(count, capacity), slot [T, K]
+    (-1 for masked or dropped entries), src_token [E*capacity] (unused rows
+    are not written)."""
     _need(topk_idx, "topk_idx", _I32)
     _debug_check_ids(topk_idx, num_experts)
     if topk_idx.dim() != 2:
@@ -112,8 +124,13 @@ def ep_dispatch_layout_padded(topk_idx, num_experts, capacity, recv_expert_count
 
 def ep_dispatch(x, slot, topk_weights, format, recv_x, recv_scale=None, recv_weight=None, stream=None,
                 num_rows=None):
-    """num_rows: rows of the receive buffers (T*K by default; E*capacity for
-    a padded slot)."""
+    """Copy every token x [T, H] (bf16) into its K receive rows given by slot:
+    EP_RECV_FP8_E4M3_G128 writes E4M3FN codes to recv_x (uint8 [rows, H])
+    and one float32 scale per 128 channels to recv_scale [rows, H/128];
+    EP_RECV_BF16 copies the bf16 bits to recv_x (bf16 [rows, H]).
+    recv_weight [rows] (optional) receives topk_weights[t, k].  num_rows:
+    rows of the receive buffers (T*K by default; E*capacity for a padded
+    slot)."""
     _need(x, "x", _BF16)
     if x.dim() != 2:
         raise ValueError("x must be [T, H]")
@@ -196,7 +213,10 @@ def ep_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format,
 
 
 def ep_combine(y, slot, topk_weights, out, stream=None, num_rows=None):
-    """num_rows: rows of y (T*K by default; E*capacity for a padded slot)."""
+    """out[t] = BF16(sum over k of topk_weights[t, k] * y[slot[t, k]]), in
+    binary32, ascending k, each product rounded before it is added.
+    y: bf16 [rows, H] in receive order; out: bf16 [T, H].  num_rows: rows
+    of y (T*K by default; E*capacity for a padded slot)."""
     _need(slot, "slot", _I32)
     if slot.dim() != 2:
         raise ValueError("slot must be [T, K]")
@@ -251,6 +271,9 @@ def ep_combine_backward(grad_out, y, slot, topk_weights, grad_y, grad_w=None, st
 
 
 def ep_cast_fp8_e4m3(inp, out, stream=None):
+    """The binary32 -> E4M3FN conversion dispatch uses (round to nearest
+    even, saturating at +-448), elementwise: inp float32, out uint8 of the
+    same shape."""
     _need(inp, "in", _F32)
     _need(out, "out", _U8, tuple(inp.shape))
     check("ep_cast_fp8_e4m3", LIB.ep_cast_fp8_e4m3(inp.data_ptr(), out.data_ptr(), inp.numel(),
