@@ -528,7 +528,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the path is one GPU's share with every expert resident in its "
-              "HBM, and this build has no multi-GPU transport (requested --gpus %d, WORLD_SIZE %d)"
+              "HBM, and this library has no multi-GPU transport (requested --gpus %d, WORLD_SIZE %d)"
               % (args.gpus, world), file=sys.stderr)
         return 2
 
