@@ -1,7 +1,7 @@
 """One step through the C ABI from plain C (tests/c_abi/ep_step: the HIP
 runtime and libep.so, no Python), bit-exact against the oracle.
 
-The driver reads seeded inputs from files, runs the layout call and
+The C program reads seeded inputs from files, runs the layout call and
 ep_dispatch (or ep_layout_dispatch), then ep_combine, and writes every
 output back; this test compares them with the oracle's.
 """
