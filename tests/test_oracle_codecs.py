@@ -46,6 +46,18 @@ def test_e4m3_saturation_and_ties():
     assert enc1(np.nextafter(np.float32(2.0 ** -10), np.float32(1))) == 0x01
 
 
+def test_e4m3_bytes_read_as_torch_float8():
+    """The receive bytes are OCP E4M3FN, the encoding of torch's
+    float8_e4m3fn: all 256 codes, viewed as that dtype, decode to the
+    oracle's values (the two NaN codes to NaN)."""
+    codes = np.arange(256, dtype=np.uint8)
+    via_torch = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    ours = e4m3_to_f32(codes)
+    nan = np.isnan(ours)
+    assert np.array_equal(np.isnan(via_torch), nan) and nan.sum() == 2
+    assert np.array_equal(via_torch[~nan].view(np.uint32), ours[~nan].view(np.uint32))
+
+
 def test_e4m3_tails_are_constant():
     """Outside [2**-12, 2**10) the code depends only on the sign: below 2**-12
     a value is under half the smallest subnormal (2**-10), so it rounds to
