@@ -172,7 +172,7 @@ def test_fallback_paths(gpu, T, K, cap):
     check_fused(gpu, idx, x, w, E, cap, True)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(48))
 def test_random(gpu, seed):
     rng = np.random.default_rng(5000 + seed)
     E = int(rng.choice([1, 5, 64, 256, 1024]))
