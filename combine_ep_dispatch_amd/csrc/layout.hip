@@ -39,7 +39,8 @@
 namespace ep {
 namespace {
 
-constexpr int kSingleMaxThreads = 1024;
+constexpr int kSingleMaxWaves = 8;  // the single-workgroup path launches at most 8 waves
+constexpr int kSingleMaxThreads = kSingleMaxWaves * 64;
 constexpr int kSingleMaxEntries = 1024;  // one workgroup, no workspace
 constexpr int kFusedMaxEntries = 65536;   // one launch, no workspace
 constexpr int kMultiThreads = 256;
@@ -389,7 +390,7 @@ size_t single_lds_bytes(int nw, int E) {
 int single_waves(int E) {
   // 8 waves: measured a little faster than 16 at 1024 entries (fewer waves
   // to scan per key, two 64-entry steps each)
-  int nw = 8;
+  int nw = kSingleMaxWaves;
   while (nw > 1 && single_lds_bytes(nw, E) > kLdsLimit) nw >>= 1;
   return nw;
 }
