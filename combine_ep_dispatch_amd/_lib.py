@@ -24,9 +24,12 @@ EXPORTS = (
     "ep_status_string",
     "ep_layout_workspace_bytes",
     "ep_dispatch_layout",
+    "ep_dispatch_layout_i64",
     "ep_dispatch_layout_padded",
+    "ep_dispatch_layout_padded_i64",
     "ep_dispatch",
     "ep_layout_dispatch",
+    "ep_layout_dispatch_i64",
     "ep_combine",
     "ep_dispatch_backward",
     "ep_combine_backward",
@@ -55,14 +58,16 @@ def _load():
     lib.ep_status_string.restype = ctypes.c_char_p
     lib.ep_layout_workspace_bytes.argtypes = [i64, i32, i32]
     lib.ep_layout_workspace_bytes.restype = sz
-    lib.ep_dispatch_layout.argtypes = [p, i64, i32, i32, p, p, p, p, p, sz, p]
-    lib.ep_dispatch_layout.restype = ctypes.c_int
-    lib.ep_dispatch_layout_padded.argtypes = [p, i64, i32, i32, i32, p, p, p, p, sz, p]
-    lib.ep_dispatch_layout_padded.restype = ctypes.c_int
+    for suffix in ("", "_i64"):
+        getattr(lib, "ep_dispatch_layout" + suffix).argtypes = [p, i64, i32, i32, p, p, p, p, p, sz, p]
+        getattr(lib, "ep_dispatch_layout" + suffix).restype = ctypes.c_int
+        getattr(lib, "ep_dispatch_layout_padded" + suffix).argtypes = [p, i64, i32, i32, i32, p, p, p, p, sz, p]
+        getattr(lib, "ep_dispatch_layout_padded" + suffix).restype = ctypes.c_int
+        getattr(lib, "ep_layout_dispatch" + suffix).argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p,
+                                                                p, p, p, sz, p]
+        getattr(lib, "ep_layout_dispatch" + suffix).restype = ctypes.c_int
     lib.ep_dispatch.argtypes = [p, i64, i32, i32, p, p, i32, p, p, p, p]
     lib.ep_dispatch.restype = ctypes.c_int
-    lib.ep_layout_dispatch.argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p, p, p, p, sz, p]
-    lib.ep_layout_dispatch.restype = ctypes.c_int
     lib.ep_combine.argtypes = [p, p, p, i64, i32, i32, p, p]
     lib.ep_combine.restype = ctypes.c_int
     lib.ep_dispatch_backward.argtypes = [p, p, i64, i32, i32, p, p]

@@ -60,6 +60,20 @@ def _need(t, name, dtypes, shape=None):
 
 
 _I32 = (torch.int32,)
+_IDX = (torch.int32, torch.int64)  # expert ids: int32, or int64 as routers produce them
+
+
+def _ids_fn(name, topk_idx):
+    """The C entry point for these ids: NAME, or NAME_i64 for int64 ids."""
+    return getattr(LIB, name + "_i64") if topk_idx.dtype == torch.int64 else getattr(LIB, name)
+
+
+def _as_ids(topk_idx):
+    """int32 and int64 ids go to the library as they are; other integer
+    types are widened to int32."""
+    if topk_idx.dtype not in _IDX:
+        topk_idx = topk_idx.to(torch.int32)
+    return topk_idx.contiguous()
 _F32 = (torch.float32,)
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 _U8 = (torch.uint8, torch.float8_e4m3fn)
@@ -79,7 +93,7 @@ def ep_dispatch_layout(topk_idx, num_experts, tokens_per_expert, expert_offset, 
     expert_offset[E]).  Rows of one expert are in ascending token order.
     workspace: uint8/int32 device tensor of ep_layout_workspace_bytes bytes
     (only needed past 65536 entries)."""
-    _need(topk_idx, "topk_idx", _I32)
+    _need(topk_idx, "topk_idx", _IDX)
     _debug_check_ids(topk_idx, num_experts)
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [T, K]")
@@ -93,7 +107,7 @@ def ep_dispatch_layout(topk_idx, num_experts, tokens_per_expert, expert_offset, 
     if workspace is not None:
         _need(workspace, "workspace", (torch.uint8, torch.int32))
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    check("ep_dispatch_layout", LIB.ep_dispatch_layout(
+    check("ep_dispatch_layout", _ids_fn("ep_dispatch_layout", topk_idx)(
         topk_idx.data_ptr(), T, K, E, tokens_per_expert.data_ptr(), expert_offset.data_ptr(),
         slot.data_ptr(), src_token.data_ptr(), ws_ptr, ws_bytes, _stream(stream)))
 
@@ -104,7 +118,7 @@ def ep_dispatch_layout_padded(topk_idx, num_experts, capacity, recv_expert_count
     capacity - 1; recv_expert_count [E] = min(count, capacity), slot [T, K]
     (-1 for masked or dropped entries), src_token [E*capacity] (unused rows
     are not written)."""
-    _need(topk_idx, "topk_idx", _I32)
+    _need(topk_idx, "topk_idx", _IDX)
     _debug_check_ids(topk_idx, num_experts)
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [T, K]")
@@ -117,7 +131,7 @@ def ep_dispatch_layout_padded(topk_idx, num_experts, capacity, recv_expert_count
     if workspace is not None:
         _need(workspace, "workspace", (torch.uint8, torch.int32))
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    check("ep_dispatch_layout_padded", LIB.ep_dispatch_layout_padded(
+    check("ep_dispatch_layout_padded", _ids_fn("ep_dispatch_layout_padded", topk_idx)(
         topk_idx.data_ptr(), T, K, E, cap, recv_expert_count.data_ptr(), slot.data_ptr(), src_token.data_ptr(),
         ws_ptr, ws_bytes, _stream(stream)))
 
@@ -167,7 +181,7 @@ def ep_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format,
     capacity 0: packed layout (expert_offset [E+1], src_token [T*K], T*K
     receive rows); capacity > 0: padded layout (expert_offset None,
     src_token [E*capacity], E*capacity receive rows)."""
-    _need(topk_idx, "topk_idx", _I32)
+    _need(topk_idx, "topk_idx", _IDX)
     _debug_check_ids(topk_idx, num_experts)
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [T, K]")
@@ -204,7 +218,7 @@ def ep_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format,
     if workspace is not None:
         _need(workspace, "workspace", (torch.uint8, torch.int32))
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    check("ep_layout_dispatch", LIB.ep_layout_dispatch(
+    check("ep_layout_dispatch", _ids_fn("ep_layout_dispatch", topk_idx)(
         topk_idx.data_ptr(), x.data_ptr(), topk_weights.data_ptr() if topk_weights is not None else None, T, H, K,
         E, cap, int(format), tokens_per_expert.data_ptr(),
         expert_offset.data_ptr() if expert_offset is not None else None, slot.data_ptr(), src_token.data_ptr(),
@@ -284,9 +298,7 @@ def ep_cast_fp8_e4m3(inp, out, stream=None):
 
 def layout(topk_idx, num_experts, stream=None):
     """Routing layout of ``topk_idx`` [T, K] (int32 or int64) -> Handle."""
-    if topk_idx.dtype != torch.int32:
-        topk_idx = topk_idx.to(torch.int32)
-    topk_idx = topk_idx.contiguous()
+    topk_idx = _as_ids(topk_idx)
     T, K = topk_idx.shape
     E = int(num_experts)
     if not 1 <= E <= EP_MAX_EXPERTS or not 1 <= K <= EP_MAX_TOPK:
@@ -314,9 +326,7 @@ def dispatch(x, topk_idx, topk_weights, num_experts, fp8=True, handle=None, stre
     T, H = x.shape
     dev = x.device
     if handle is None:
-        if topk_idx.dtype != torch.int32:
-            topk_idx = topk_idx.to(torch.int32)
-        topk_idx = topk_idx.contiguous()
+        topk_idx = _as_ids(topk_idx)
     K = handle.slot.shape[1] if handle is not None else topk_idx.shape[1]
     recv_weight = None
     if topk_weights is not None:
@@ -357,9 +367,7 @@ def combine(y, handle, topk_weights, stream=None):
 
 def layout_padded(topk_idx, num_experts, capacity, stream=None):
     """Low-latency layout with ``capacity`` rows per expert -> PaddedHandle."""
-    if topk_idx.dtype != torch.int32:
-        topk_idx = topk_idx.to(torch.int32)
-    topk_idx = topk_idx.contiguous()
+    topk_idx = _as_ids(topk_idx)
     T, K = topk_idx.shape
     E, cap = int(num_experts), int(capacity)
     dev = topk_idx.device
@@ -380,9 +388,7 @@ def low_latency_dispatch(x, topk_idx, num_max_tokens, num_experts, fp8=True, str
     Returns (recv_x [E, num_max_tokens, H], recv_scale [E, num_max_tokens,
     H/128] or None, recv_expert_count [E], handle).
     """
-    if topk_idx.dtype != torch.int32:
-        topk_idx = topk_idx.to(torch.int32)
-    topk_idx = topk_idx.contiguous()
+    topk_idx = _as_ids(topk_idx)
     T, H = x.shape
     K = topk_idx.shape[1]
     E, cap = int(num_experts), int(num_max_tokens)

@@ -29,7 +29,8 @@ ep_status check_common(int64_t T, int32_t K) {
 
 // Checks of the layout arguments (capacity 0: packed layout with offsets;
 // capacity > 0: padded layout, offsets unused).
-ep_status check_layout(const int32_t* topk_idx, int64_t T, int32_t K, int32_t E, int32_t capacity,
+// id_bytes: width of one expert id (4 or 8); the ids must be aligned to it.
+ep_status check_layout(const void* topk_idx, size_t id_bytes, int64_t T, int32_t K, int32_t E, int32_t capacity,
                        const int32_t* counts, const int32_t* offsets, const int32_t* slot, const int32_t* src,
                        const void* workspace, size_t workspace_bytes) {
   ep_status st = check_common(T, K);
@@ -46,7 +47,7 @@ ep_status check_layout(const int32_t* topk_idx, int64_t T, int32_t K, int32_t E,
   const int64_t rows = T * K;
   if (rows > 0) {
     if (!topk_idx || !slot || !src) return EP_ERR_INVALID_ARG;
-    if (!aligned(topk_idx, 4) || !aligned(slot, 4) || !aligned(src, 4)) return EP_ERR_INVALID_ARG;
+    if (!aligned(topk_idx, id_bytes) || !aligned(slot, 4) || !aligned(src, 4)) return EP_ERR_INVALID_ARG;
   }
   const size_t need = ep::layout_workspace_bytes(rows, E);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
@@ -92,31 +93,67 @@ EP_API size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t top_k, int32
   return ep::layout_workspace_bytes(num_tokens * top_k, num_experts);
 }
 
-EP_API ep_status ep_dispatch_layout(const int32_t* topk_idx, int64_t num_tokens, int32_t top_k,
-                                    int32_t num_experts, int32_t* tokens_per_expert, int32_t* expert_offset,
-                                    int32_t* slot, int32_t* src_token, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
-  ep_status st = check_layout(topk_idx, num_tokens, top_k, num_experts, 0, tokens_per_expert, expert_offset, slot,
-                              src_token, workspace, workspace_bytes);
+namespace {
+
+template <typename Idx>
+ep_status dispatch_layout(const Idx* topk_idx, int64_t num_tokens, int32_t top_k, int32_t num_experts,
+                          int32_t* tokens_per_expert, int32_t* expert_offset, int32_t* slot, int32_t* src_token,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  ep_status st = check_layout(topk_idx, sizeof(Idx), num_tokens, top_k, num_experts, 0, tokens_per_expert,
+                              expert_offset, slot, src_token, workspace, workspace_bytes);
   if (st != EP_OK) return st;
   return from_hip(ep::launch_layout(topk_idx, static_cast<int32_t>(num_tokens * top_k), top_k, num_experts, 0,
                                     tokens_per_expert, expert_offset, slot, src_token, workspace,
                                     static_cast<hipStream_t>(stream)));
 }
 
-EP_API ep_status ep_dispatch_layout_padded(const int32_t* topk_idx, int64_t num_tokens, int32_t top_k,
-                                           int32_t num_experts, int32_t capacity, int32_t* recv_expert_count,
-                                           int32_t* slot, int32_t* src_token, void* workspace,
-                                           size_t workspace_bytes, void* stream) {
+template <typename Idx>
+ep_status dispatch_layout_padded(const Idx* topk_idx, int64_t num_tokens, int32_t top_k, int32_t num_experts,
+                                 int32_t capacity, int32_t* recv_expert_count, int32_t* slot, int32_t* src_token,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   ep_status st = check_common(num_tokens, top_k);
   if (st != EP_OK) return st;
   if (capacity < 1) return EP_ERR_INVALID_ARG;
-  st = check_layout(topk_idx, num_tokens, top_k, num_experts, capacity, recv_expert_count, nullptr, slot,
-                    src_token, workspace, workspace_bytes);
+  st = check_layout(topk_idx, sizeof(Idx), num_tokens, top_k, num_experts, capacity, recv_expert_count, nullptr,
+                    slot, src_token, workspace, workspace_bytes);
   if (st != EP_OK) return st;
   return from_hip(ep::launch_layout(topk_idx, static_cast<int32_t>(num_tokens * top_k), top_k, num_experts,
                                     capacity, recv_expert_count, nullptr, slot, src_token, workspace,
                                     static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+EP_API ep_status ep_dispatch_layout(const int32_t* topk_idx, int64_t num_tokens, int32_t top_k,
+                                    int32_t num_experts, int32_t* tokens_per_expert, int32_t* expert_offset,
+                                    int32_t* slot, int32_t* src_token, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return dispatch_layout(topk_idx, num_tokens, top_k, num_experts, tokens_per_expert, expert_offset, slot,
+                         src_token, workspace, workspace_bytes, stream);
+}
+
+EP_API ep_status ep_dispatch_layout_i64(const int64_t* topk_idx, int64_t num_tokens, int32_t top_k,
+                                        int32_t num_experts, int32_t* tokens_per_expert, int32_t* expert_offset,
+                                        int32_t* slot, int32_t* src_token, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return dispatch_layout(topk_idx, num_tokens, top_k, num_experts, tokens_per_expert, expert_offset, slot,
+                         src_token, workspace, workspace_bytes, stream);
+}
+
+EP_API ep_status ep_dispatch_layout_padded(const int32_t* topk_idx, int64_t num_tokens, int32_t top_k,
+                                           int32_t num_experts, int32_t capacity, int32_t* recv_expert_count,
+                                           int32_t* slot, int32_t* src_token, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  return dispatch_layout_padded(topk_idx, num_tokens, top_k, num_experts, capacity, recv_expert_count, slot,
+                                src_token, workspace, workspace_bytes, stream);
+}
+
+EP_API ep_status ep_dispatch_layout_padded_i64(const int64_t* topk_idx, int64_t num_tokens, int32_t top_k,
+                                               int32_t num_experts, int32_t capacity, int32_t* recv_expert_count,
+                                               int32_t* slot, int32_t* src_token, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+  return dispatch_layout_padded(topk_idx, num_tokens, top_k, num_experts, capacity, recv_expert_count, slot,
+                                src_token, workspace, workspace_bytes, stream);
 }
 
 EP_API ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, int32_t top_k,
@@ -136,13 +173,15 @@ EP_API ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, 
                                            topk_weights, static_cast<uint16_t*>(recv_x), recv_weight, s));
 }
 
-EP_API ep_status ep_layout_dispatch(const int32_t* topk_idx, const void* x, const float* topk_weights,
-                                    int64_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
-                                    int32_t capacity, int32_t format, int32_t* tokens_per_expert,
-                                    int32_t* expert_offset, int32_t* slot, int32_t* src_token, void* recv_x,
-                                    float* recv_scale, float* recv_weight, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
-  ep_status st = check_layout(topk_idx, num_tokens, top_k, num_experts, capacity, tokens_per_expert,
+namespace {
+
+template <typename Idx>
+ep_status layout_dispatch(const Idx* topk_idx, const void* x, const float* topk_weights, int64_t num_tokens,
+                          int32_t hidden, int32_t top_k, int32_t num_experts, int32_t capacity, int32_t format,
+                          int32_t* tokens_per_expert, int32_t* expert_offset, int32_t* slot, int32_t* src_token,
+                          void* recv_x, float* recv_scale, float* recv_weight, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  ep_status st = check_layout(topk_idx, sizeof(Idx), num_tokens, top_k, num_experts, capacity, tokens_per_expert,
                               capacity == 0 ? expert_offset : nullptr, slot, src_token, workspace,
                               workspace_bytes);
   if (st != EP_OK) return st;
@@ -153,6 +192,30 @@ EP_API ep_status ep_layout_dispatch(const int32_t* topk_idx, const void* x, cons
       num_experts, capacity, format == EP_RECV_FP8_E4M3_G128, tokens_per_expert,
       capacity == 0 ? expert_offset : nullptr, slot, src_token, recv_x, recv_scale, recv_weight, workspace,
       static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+EP_API ep_status ep_layout_dispatch(const int32_t* topk_idx, const void* x, const float* topk_weights,
+                                    int64_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
+                                    int32_t capacity, int32_t format, int32_t* tokens_per_expert,
+                                    int32_t* expert_offset, int32_t* slot, int32_t* src_token, void* recv_x,
+                                    float* recv_scale, float* recv_weight, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return layout_dispatch(topk_idx, x, topk_weights, num_tokens, hidden, top_k, num_experts, capacity, format,
+                         tokens_per_expert, expert_offset, slot, src_token, recv_x, recv_scale, recv_weight,
+                         workspace, workspace_bytes, stream);
+}
+
+EP_API ep_status ep_layout_dispatch_i64(const int64_t* topk_idx, const void* x, const float* topk_weights,
+                                        int64_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
+                                        int32_t capacity, int32_t format, int32_t* tokens_per_expert,
+                                        int32_t* expert_offset, int32_t* slot, int32_t* src_token, void* recv_x,
+                                        float* recv_scale, float* recv_weight, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return layout_dispatch(topk_idx, x, topk_weights, num_tokens, hidden, top_k, num_experts, capacity, format,
+                         tokens_per_expert, expert_offset, slot, src_token, recv_x, recv_scale, recv_weight,
+                         workspace, workspace_bytes, stream);
 }
 
 EP_API ep_status ep_combine(const void* y, const int32_t* slot, const float* topk_weights, int64_t num_tokens,

@@ -35,6 +35,14 @@ __device__ __forceinline__ uint32_t max8_u32(uint32_t v) {
   return v;
 }
 
+// The key of an expert id (int32 or int64): the id itself inside [0, E),
+// otherwise E (a masked entry).  Every kernel turns ids into keys as it
+// loads them, so wide ids never meet 32-bit arithmetic.
+template <typename Idx>
+__device__ __forceinline__ int expert_key(Idx e, int E) {
+  return (e >= 0 && e < static_cast<Idx>(E)) ? static_cast<int>(e) : E;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
   const int lane = threadIdx.x & (kWave - 1);

@@ -13,9 +13,11 @@ namespace ep {
 size_t layout_workspace_bytes(int64_t rows, int32_t num_experts);
 // capacity == 0: packed layout (counts, offsets, slot, src[T*K]);
 // capacity  > 0: padded layout (counts clamped, offsets unused, src[E*capacity]).
-hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, int32_t num_experts,
-                         int32_t capacity, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
-                         void* workspace, hipStream_t stream);
+// Idx: int32_t or int64_t expert ids.
+template <typename Idx>
+hipError_t launch_layout(const Idx* topk_idx, int32_t rows, int32_t top_k, int32_t num_experts, int32_t capacity,
+                         int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src, void* workspace,
+                         hipStream_t stream);
 
 hipError_t launch_dispatch_fp8(const uint16_t* x, int32_t num_tokens, int32_t hidden, int32_t top_k,
                                const int32_t* slot, const float* topk_weights, uint8_t* recv,
@@ -39,7 +41,8 @@ hipError_t launch_combine_backward(const uint16_t* grad_out, const uint16_t* y, 
 // num_tokens * top_k <= kFusedMaxEntries, else launch_layout followed by the
 // dispatch kernel (then `workspace` must hold layout_workspace_bytes).
 constexpr int kFusedMaxEntries = 3072;
-hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, const float* topk_weights,
+template <typename Idx>
+hipError_t launch_layout_dispatch(const Idx* topk_idx, const uint16_t* x, const float* topk_weights,
                                   int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
                                   int32_t capacity, bool fp8, int32_t* counts, int32_t* offsets, int32_t* slot,
                                   int32_t* src, void* recv, float* recv_scale, float* recv_weight,

@@ -57,35 +57,41 @@ static_assert(static_cast<int64_t>(1025) * kFusedMaxEntries < (int64_t(1) << 31)
 constexpr int kTokenLdsInts = kMaxWaves * kMaxK + 2 * kMaxK;
 constexpr int kLdsInts = 1025 + kMaxWaves > kTokenLdsInts ? 1025 + kMaxWaves : kTokenLdsInts;
 
-__device__ __forceinline__ int key_of(int e, int E) { return (e >= 0 && e < E) ? e : E; }
-
-// This lane's ids: entries u*blockDim + tid for u < NS, with the address
+// This lane's keys: entries u*blockDim + tid for u < NS, with the address
 // clamped to the last entry (n >= 1) so that all NS loads are issued back
-// to back, free of branches; lanes past n get a copy of the last id, which
+// to back, free of branches; lanes past n get a copy of the last key, which
 // callers mask by position.
-template <int NS>
-__device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int n, int (&e)[NS]) {
+template <int NS, typename Idx>
+__device__ __forceinline__ void load_ids(const Idx* __restrict__ idx, int n, Idx (&raw)[NS]) {
   const int bs = blockDim.x;
 #pragma unroll
-  for (int u = 0; u < NS; ++u) e[u] = idx[min(u * bs + static_cast<int>(threadIdx.x), n - 1)];
+  for (int u = 0; u < NS; ++u) raw[u] = idx[min(u * bs + static_cast<int>(threadIdx.x), n - 1)];
+}
+
+template <int NS, typename Idx>
+__device__ __forceinline__ void load_keys(const Idx* __restrict__ idx, int n, int E, int (&e)[NS]) {
+  Idx raw[NS];
+  load_ids<NS>(idx, n, raw);
+#pragma unroll
+  for (int u = 0; u < NS; ++u) e[u] = expert_key(raw[u], E);
 }
 
 // Workgroup 0: per-expert counts (clamped to the capacity in the padded
 // layout) and, for the packed layout, the exclusive-scan offsets.
-template <int NS>
-__device__ void write_counts_block(const int32_t* __restrict__ idx, int n, int E, int cap, int* lds,
+template <int NS, typename Idx>
+__device__ void write_counts_block(const Idx* __restrict__ idx, int n, int E, int cap, int* lds,
                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
   const int tid = threadIdx.x, bs = blockDim.x, nk = E + 1;
   int* hist = lds;
   int* wave_tot = lds + nk;
-  int e[NS];
-  if (n > 0) load_ids<NS>(idx, n, e);  // block-uniform; nothing to read for an empty batch
+  int e[NS];  // keys
+  if (n > 0) load_keys<NS>(idx, n, E, e);  // block-uniform; nothing to read for an empty batch
   for (int i = tid; i < nk; i += bs) hist[i] = 0;
   __syncthreads();
   if (n > 0) {
 #pragma unroll
     for (int u = 0; u < NS; ++u)
-      if (u * bs + tid < n) atomicAdd(&hist[key_of(e[u], E)], 1);
+      if (u * bs + tid < n) atomicAdd(&hist[e[u]], 1);
   }
   __syncthreads();
   for (int j = tid; j < E; j += bs) counts[j] = cap == 0 ? hist[j] : min(hist[j], cap);
@@ -95,7 +101,7 @@ __device__ void write_counts_block(const int32_t* __restrict__ idx, int n, int E
   }
 }
 
-// Per-wave counts for targets k0 .. k0+KC-1 (expert ids te) of the token
+// Per-wave counts for targets k0 .. k0+KC-1 (keys te) of the token
 // whose entries start at p0, as one unsigned comparison per entry:
 //   packed: c_j = #{entries with lo_j <= code < code_j}, lo_j = 0: the row;
 //   padded: the same with lo_j = key_j * n: the rank among entries with the
@@ -111,7 +117,7 @@ __device__ __forceinline__ void count_targets(const int (&te)[KC], int p0, int k
   int tk[KC], lo[KC], span[KC], c[KC];
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
-    tk[j] = k0 + j < K ? key_of(te[j], E) : E;
+    tk[j] = k0 + j < K ? te[j] : E;
     lo[j] = padded ? tk[j] * n : 0;
     span[j] = tk[j] * n + p0 + k0 + j - lo[j];
     c[j] = 0;
@@ -137,9 +143,10 @@ __device__ __forceinline__ void count_targets(const int (&te)[KC], int p0, int k
 // NS: steps of blockDim entries per lane (n <= NS * blockDim).  MAXT: the
 // largest workgroup the instantiation is launched with (256, or 1024 for
 // token-wide workgroups); the tighter bound measured 0.25-0.45 us faster.
-template <int KT, bool FP8, int NS, int MAXT>
+// Idx: int32_t or int64_t expert ids.
+template <int KT, bool FP8, int NS, int MAXT, typename Idx>
 __global__ __launch_bounds__(MAXT) void layout_dispatch_kernel(
-    const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, const float* __restrict__ w, int32_t T,
+    const Idx* __restrict__ idx, const uint16_t* __restrict__ x, const float* __restrict__ w, int32_t T,
     int32_t H, int32_t Krt, int32_t E, int32_t cap, uint32_t nchunk, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src, void* __restrict__ recv,
     float* __restrict__ recv_scale, float* __restrict__ recv_weight) {
@@ -164,9 +171,9 @@ __global__ __launch_bounds__(MAXT) void layout_dispatch_kernel(
   // latency overlaps the counting), then all ids.  The token is read with
   // plain loads: at these sizes it is usually still in the caches (measured
   // 5.7 against 6.0 us with streaming loads at 128 tokens)
-  int te[KC];
+  int te[KC];  // the token's keys
 #pragma unroll
-  for (int j = 0; j < KC; ++j) te[j] = idx[p0 + min(j, K - 1)];
+  for (int j = 0; j < KC; ++j) te[j] = expert_key(idx[p0 + min(j, K - 1)], E);
   u32x4 a = {0, 0, 0, 0}, a2 = {0, 0, 0, 0};
   if (active) {
     const u32x4* px = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * H);
@@ -177,15 +184,16 @@ __global__ __launch_bounds__(MAXT) void layout_dispatch_kernel(
       a = px[v];
     }
   }
-  int code[NS];
-  load_ids<NS>(idx, n, code);
+  Idx raw[NS];
+  load_ids<NS>(idx, n, raw);
   // keep every load above this point: the compiler would otherwise sink
   // some of them next to their first use, one memory latency after another
   asm volatile("" ::: "memory");
+  int code[NS];
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
     const int p = u * bs + tid;
-    code[u] = p < n ? key_of(code[u], E) * n + p : 0x7FFFFFFF;
+    code[u] = p < n ? expert_key(raw[u], E) * n + p : 0x7FFFFFFF;
   }
 
   const int nsteps = (n + bs - 1) / bs;
@@ -196,7 +204,7 @@ __global__ __launch_bounds__(MAXT) void layout_dispatch_kernel(
   count_targets<KC, NS>(te, p0, 0, K, n, E, padded, code, nsteps, wc, tkey);
   for (int k0 = KC; k0 < K; k0 += KC) {  // top-k beyond one pass (generic K only)
 #pragma unroll
-    for (int j = 0; j < KC; ++j) te[j] = idx[p0 + min(k0 + j, K - 1)];
+    for (int j = 0; j < KC; ++j) te[j] = expert_key(idx[p0 + min(k0 + j, K - 1)], E);
     count_targets<KC, NS>(te, p0, k0, K, n, E, padded, code, nsteps, wc, tkey);
   }
   __syncthreads();
@@ -265,15 +273,15 @@ int fused_threads(uint32_t vpt, int n) {
   return static_cast<int>(lanes < kMinThreads ? kMinThreads : lanes > kMaxThreads ? kMaxThreads : lanes);
 }
 
-template <bool FP8, int NS, int MAXT>
-void launch_fused(const int32_t* idx, const uint16_t* x, const float* w, int32_t T, int32_t H, int32_t K,
+template <bool FP8, int NS, int MAXT, typename Idx>
+void launch_fused(const Idx* idx, const uint16_t* x, const float* w, int32_t T, int32_t H, int32_t K,
                   int32_t E, int32_t cap, int bs, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
                   void* recv, float* recv_scale, float* recv_weight, hipStream_t stream) {
   const uint32_t vpt = static_cast<uint32_t>(H) / (FP8 ? 16 : 8);
   const uint32_t nchunk = (vpt + bs - 1) / bs;
   const dim3 grid(1 + static_cast<uint32_t>(T) * nchunk), block(bs);
 #define EP_FUSED(KV)                                                                                            \
-  hipLaunchKernelGGL((layout_dispatch_kernel<KV, FP8, NS, MAXT>), grid, block, 0, stream, idx, x, w, T, H, K, E, cap, \
+  hipLaunchKernelGGL((layout_dispatch_kernel<KV, FP8, NS, MAXT, Idx>), grid, block, 0, stream, idx, x, w, T, H, K, E, cap, \
                      nchunk, counts, offsets, slot, src, recv, recv_scale, recv_weight)
   switch (K) {
     case 1: EP_FUSED(1); break;
@@ -286,8 +294,8 @@ void launch_fused(const int32_t* idx, const uint16_t* x, const float* w, int32_t
 #undef EP_FUSED
 }
 
-template <bool FP8>
-void launch_fused_ns(const int32_t* idx, const uint16_t* x, const float* w, int32_t T, int32_t H, int32_t K,
+template <bool FP8, typename Idx>
+void launch_fused_ns(const Idx* idx, const uint16_t* x, const float* w, int32_t T, int32_t H, int32_t K,
                      int32_t E, int32_t cap, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
                      void* recv, float* recv_scale, float* recv_weight, hipStream_t stream) {
   static_assert(kFusedMaxEntries <= 12 * kMinThreads, "steps per lane");
@@ -319,7 +327,8 @@ void launch_fused_ns(const int32_t* idx, const uint16_t* x, const float* w, int3
 
 }  // namespace
 
-hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, const float* topk_weights,
+template <typename Idx>
+hipError_t launch_layout_dispatch(const Idx* topk_idx, const uint16_t* x, const float* topk_weights,
                                   int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
                                   int32_t capacity, bool fp8, int32_t* counts, int32_t* offsets, int32_t* slot,
                                   int32_t* src, void* recv, float* recv_scale, float* recv_weight,
@@ -342,5 +351,12 @@ hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, co
                            offsets, slot, src, recv, recv_scale, recv_weight, stream);
   return hipGetLastError();
 }
+
+template hipError_t launch_layout_dispatch<int32_t>(const int32_t*, const uint16_t*, const float*, int32_t, int32_t,
+                                                    int32_t, int32_t, int32_t, bool, int32_t*, int32_t*, int32_t*,
+                                                    int32_t*, void*, float*, float*, void*, hipStream_t);
+template hipError_t launch_layout_dispatch<int64_t>(const int64_t*, const uint16_t*, const float*, int32_t, int32_t,
+                                                    int32_t, int32_t, int32_t, bool, int32_t*, int32_t*, int32_t*,
+                                                    int32_t*, void*, float*, float*, void*, hipStream_t);
 
 }  // namespace ep

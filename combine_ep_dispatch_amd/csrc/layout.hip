@@ -58,16 +58,16 @@ constexpr int kMultiWaves = kMultiThreads / kWave;
 // those lanes below this one plus the running count; the lowest such lane
 // advances the count and clears the mask.  LDS operations of one wavefront
 // execute in program order, which is all the step relies on.
-template <int ITERS>
-__device__ __forceinline__ void rank_wave_range(const int32_t* __restrict__ idx, int p_begin, int p_end,
+template <int ITERS, typename Idx>
+__device__ __forceinline__ void rank_wave_range(const Idx* __restrict__ idx, int p_begin, int p_end,
                                                 int E, uint64_t* lmask, int* cnt, int (&key)[ITERS],
                                                 int (&rank)[ITERS]) {
   const int lane = threadIdx.x & (kWave - 1);
-  int e[ITERS];
+  int e[ITERS];  // keys
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
     const int p = p_begin + i * kWave + lane;
-    e[i] = p < p_end ? idx[p] : -1;
+    e[i] = p < p_end ? expert_key(idx[p], E) : E;
   }
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
@@ -78,7 +78,7 @@ __device__ __forceinline__ void rank_wave_range(const int32_t* __restrict__ idx,
     }
     const int p = p_begin + i * kWave + lane;
     const bool inr = p < p_end;
-    const int k = (e[i] >= 0 && e[i] < E) ? e[i] : E;
+    const int k = e[i];
     if (inr) __hip_atomic_fetch_or(&lmask[k], 1ull << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
     __builtin_amdgcn_wave_barrier();
     const uint64_t same = inr ? __hip_atomic_load(&lmask[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT) : 0ull;
@@ -131,9 +131,9 @@ __device__ __forceinline__ void write_counts(const int* off, int E, int cap, int
     for (int j = tid; j <= E; j += bs) offsets[j] = off[j];
 }
 
-template <int ITERS>
+template <int ITERS, typename Idx>
 __global__ __launch_bounds__(kSingleMaxThreads) void layout_single(
-    const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t* __restrict__ counts,
+    const Idx* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src) {
   extern __shared__ uint64_t lds64[];
   const int tid = threadIdx.x, bs = blockDim.x, nw = bs / kWave, w = tid / kWave;
@@ -176,8 +176,8 @@ __global__ __launch_bounds__(kSingleMaxThreads) void layout_single(
   }
 }
 
-template <int ITERS>
-__global__ __launch_bounds__(kMultiThreads) void layout_count(const int32_t* __restrict__ idx, int32_t R,
+template <int ITERS, typename Idx>
+__global__ __launch_bounds__(kMultiThreads) void layout_count(const Idx* __restrict__ idx, int32_t R,
                                                               int32_t E, int32_t* __restrict__ slot_tmp,
                                                               int32_t* __restrict__ hist) {
   extern __shared__ uint64_t lds64[];
@@ -216,9 +216,9 @@ __global__ __launch_bounds__(kMultiThreads) void layout_count(const int32_t* __r
   }
 }
 
-template <int ITERS>
+template <int ITERS, typename Idx>
 __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
-    const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t nblocks,
+    const Idx* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t nblocks,
     const int32_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ slot, int32_t* __restrict__ src) {
   extern __shared__ int lds[];
@@ -232,11 +232,11 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
 
   // this chunk's entries and their in-chunk ranks, loaded up front so the
   // latency overlaps the histogram loads below
-  int e[ITERS], loc[ITERS];
+  int e[ITERS], loc[ITERS];  // keys, in-chunk ranks
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
     const int p = b * kChunk + i * kMultiThreads + tid;
-    e[i] = p < R ? idx[p] : 0;
+    e[i] = p < R ? expert_key(idx[p], E) : E;
     loc[i] = p < R ? slot[p] : 0;
   }
 
@@ -264,10 +264,7 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
     const int p = b * kChunk + i * kMultiThreads + tid;
-    if (p < R) {
-      const int k = (e[i] >= 0 && e[i] < E) ? e[i] : E;
-      write_entry(p, k, base[k] + loc[i], off, E, K, cap, slot, src);
-    }
+    if (p < R) write_entry(p, e[i], base[e[i]] + loc[i], off, E, K, cap, slot, src);
   }
 }
 
@@ -280,9 +277,10 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
 // scan of the totals, and an entry's row is offset + before + (own-chunk
 // rank).  Every block reads all T*K ids (from L2 after the first), which
 // trades redundant on-chip work for the second launch and the workspace.
-template <int NW, bool V4>
+// V4: 16-byte id loads (int32 ids aligned to 16 bytes only).
+template <int NW, bool V4, typename Idx>
 __global__ __launch_bounds__(NW * kWave) void layout_fused(
-    const int32_t* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t* __restrict__ counts,
+    const Idx* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src) {
   extern __shared__ uint64_t lds64[];
   constexpr int kThreads = NW * kWave;
@@ -306,12 +304,12 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
   const int c0 = blockIdx.x * kThreads;
   const int c1 = min(R, c0 + kThreads);
   // count entry p (outside this block's chunk) into the before/after histogram
-  auto count_one = [&](int p, int e) {
+  auto count_one = [&](int p, int k) {
     if (p >= c0 && p < c1) return;
-    const int k = (e >= 0 && e < E) ? e : E;
     atomicAdd(p < c0 ? &before[k] : &after[k], 1);
   };
-  if (V4) {
+  if constexpr (V4) {
+    static_assert(sizeof(Idx) == 4, "16-byte id loads read int32 ids");
     // 16-byte loads: 4 ids each, 8 loads in flight per thread
     const int4* idx4 = reinterpret_cast<const int4*>(idx);
     const int n4 = R / 4;
@@ -327,22 +325,22 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
       for (int u = 0; u < kUnroll; ++u) {
         const int q = q0 + u * kThreads + tid;
         if (q >= n4) continue;
-        count_one(4 * q, e[u].x);
-        count_one(4 * q + 1, e[u].y);
-        count_one(4 * q + 2, e[u].z);
-        count_one(4 * q + 3, e[u].w);
+        count_one(4 * q, expert_key(e[u].x, E));
+        count_one(4 * q + 1, expert_key(e[u].y, E));
+        count_one(4 * q + 2, expert_key(e[u].z, E));
+        count_one(4 * q + 3, expert_key(e[u].w, E));
       }
     }
     const int p = 4 * n4 + tid;  // the last R % 4 ids
-    if (p < R) count_one(p, idx[p]);
+    if (p < R) count_one(p, expert_key(idx[p], E));
   } else {
     constexpr int kUnroll = 16;
     for (int q0 = 0; q0 < R; q0 += kThreads * kUnroll) {
-      int e[kUnroll];
+      int e[kUnroll];  // keys
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int p = q0 + u * kThreads + tid;
-        e[u] = p < R ? idx[p] : 0;
+        e[u] = p < R ? expert_key(idx[p], E) : E;
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -421,9 +419,10 @@ size_t layout_workspace_bytes(int64_t rows, int32_t num_experts) {
   return static_cast<size_t>(nblocks) * (num_experts + 1) * sizeof(int32_t);
 }
 
-hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, int32_t num_experts,
-                         int32_t capacity, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
-                         void* workspace, hipStream_t stream) {
+template <typename Idx>
+hipError_t launch_layout(const Idx* topk_idx, int32_t rows, int32_t top_k, int32_t num_experts, int32_t capacity,
+                         int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src, void* workspace,
+                         hipStream_t stream) {
   const int E = num_experts, nk = E + 1;
   const LayoutPath path = choose_path(rows);
   if (path == LayoutPath::kSingle) {
@@ -431,9 +430,9 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, i
     const int steps = ((rows + nw - 1) / nw + kWave - 1) / kWave;  // 64-entry steps per wave
     const size_t lds = single_lds_bytes(nw, E);
     const dim3 grid(1), block(nw * kWave);
-#define EP_LAYOUT_SINGLE(IT)                                                                     \
-  hipLaunchKernelGGL(layout_single<IT>, grid, block, lds, stream, topk_idx, rows, top_k, E, capacity, counts, \
-                     offsets, slot, src)
+#define EP_LAYOUT_SINGLE(IT)                                                                                  \
+  hipLaunchKernelGGL((layout_single<IT, Idx>), grid, block, lds, stream, topk_idx, rows, top_k, E, capacity, \
+                     counts, offsets, slot, src)
     if (steps <= 1) EP_LAYOUT_SINGLE(1);
     else if (steps <= 4) EP_LAYOUT_SINGLE(4);
     else EP_LAYOUT_SINGLE(16);
@@ -445,19 +444,23 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, i
     const int chunk = nw * kWave;
     const dim3 grid((rows + chunk - 1) / chunk), block(chunk);
     const size_t lds = fused_lds_bytes(nw, E);
-#define EP_LAYOUT_FUSED(NW)                                                                         \
-  if (v4)                                                                                           \
-    hipLaunchKernelGGL((layout_fused<NW, true>), grid, block, lds, stream, topk_idx, rows, top_k, E, capacity, \
-                       counts, offsets, slot, src);                                                 \
-  else                                                                                              \
-    hipLaunchKernelGGL((layout_fused<NW, false>), grid, block, lds, stream, topk_idx, rows, top_k, E, capacity, \
-                       counts, offsets, slot, src)
-    const bool v4 = (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0;
+    // 16-byte id loads: int32 ids aligned to 16 bytes
+    const bool v4 = sizeof(Idx) == 4 && (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0;
+#define EP_LAYOUT_FUSED_V(NW, V)                                                                                  \
+  hipLaunchKernelGGL((layout_fused<NW, V, Idx>), grid, block, lds, stream, topk_idx, rows, top_k, E, capacity, \
+                     counts, offsets, slot, src)
+#define EP_LAYOUT_FUSED(NW)                                                   \
+  if constexpr (sizeof(Idx) == 4) {                                           \
+    if (v4) EP_LAYOUT_FUSED_V(NW, true); else EP_LAYOUT_FUSED_V(NW, false);    \
+  } else {                                                                    \
+    EP_LAYOUT_FUSED_V(NW, false);                                             \
+  }
     if (nw >= 16) { EP_LAYOUT_FUSED(16); }
     else if (nw >= 8) { EP_LAYOUT_FUSED(8); }
     else if (nw >= 4) { EP_LAYOUT_FUSED(4); }
     else { EP_LAYOUT_FUSED(1); }
 #undef EP_LAYOUT_FUSED
+#undef EP_LAYOUT_FUSED_V
     return hipGetLastError();
   }
   const int chunk = kMultiThreads * kMultiIters;
@@ -466,10 +469,16 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t rows, int32_t top_k, i
   const size_t lds_count = static_cast<size_t>(kMultiWaves * nk) * (sizeof(uint64_t) + sizeof(int));
   const size_t lds_final = static_cast<size_t>(2 * nk + kMultiWaves) * sizeof(int);
   const dim3 grid(nblocks), block(kMultiThreads);
-  hipLaunchKernelGGL(layout_count<kMultiIters>, grid, block, lds_count, stream, topk_idx, rows, E, slot, hist);
-  hipLaunchKernelGGL(layout_finalize<kMultiIters>, grid, block, lds_final, stream, topk_idx, rows, top_k, E,
+  hipLaunchKernelGGL((layout_count<kMultiIters, Idx>), grid, block, lds_count, stream, topk_idx, rows, E, slot,
+                     hist);
+  hipLaunchKernelGGL((layout_finalize<kMultiIters, Idx>), grid, block, lds_final, stream, topk_idx, rows, top_k, E,
                      capacity, nblocks, hist, counts, offsets, slot, src);
   return hipGetLastError();
 }
+
+template hipError_t launch_layout<int32_t>(const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t*, int32_t*,
+                                           int32_t*, int32_t*, void*, hipStream_t);
+template hipError_t launch_layout<int64_t>(const int64_t*, int32_t, int32_t, int32_t, int32_t, int32_t*, int32_t*,
+                                           int32_t*, int32_t*, void*, hipStream_t);
 
 }  // namespace ep

@@ -18,7 +18,7 @@ class StepPlan:
     """One MoE step's buffers: routing, tokens, receive rows, expert outputs
     and the combined output.
 
-    topk_idx int32 [T, K]; topk_weights float32 [T, K]; x bf16 [T, H];
+    topk_idx int32 or int64 [T, K]; topk_weights float32 [T, K]; x bf16 [T, H];
     capacity 0 for the packed layout (T*K receive rows) or the rows per
     expert of the low-latency layout (E*capacity rows); fp8 selects the
     receive format.  y (expert outputs, bf16 [rows, H]) defaults to a new
@@ -31,7 +31,7 @@ class StepPlan:
     """
 
     def __init__(self, topk_idx, topk_weights, x, num_experts, capacity=0, fp8=True, y=None, stream=None):
-        api._need(topk_idx, "topk_idx", (torch.int32,))
+        api._need(topk_idx, "topk_idx", api._IDX)
         if topk_idx.dim() != 2:
             raise ValueError("topk_idx must be [T, K]")
         T, K = topk_idx.shape
@@ -68,7 +68,11 @@ class StepPlan:
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.stream = api._stream(stream)
 
-        # argument tuples are built once; the C side still rejects a bad one
+        # entry points for these ids, and argument tuples built once; the C
+        # side still rejects a bad one
+        self._fn_layout = api._ids_fn("ep_dispatch_layout", topk_idx)
+        self._fn_layout_padded = api._ids_fn("ep_dispatch_layout_padded", topk_idx)
+        self._fn_layout_dispatch = api._ids_fn("ep_layout_dispatch", topk_idx)
         self._layout_args = self._make_layout_args()
         self._dispatch_args = (x.data_ptr(), T, H, K, self.slot.data_ptr(), None, self.fmt, self.recv_x.data_ptr(),
                                self.recv_scale.data_ptr() if self.recv_scale is not None else None, None,
@@ -96,16 +100,16 @@ class StepPlan:
     def layout(self):
         padded, args = self._layout_args
         if padded:
-            check("ep_dispatch_layout_padded", LIB.ep_dispatch_layout_padded(*args))
+            check("ep_dispatch_layout_padded", self._fn_layout_padded(*args))
         else:
-            check("ep_dispatch_layout", LIB.ep_dispatch_layout(*args))
+            check("ep_dispatch_layout", self._fn_layout(*args))
 
     def dispatch(self):
         check("ep_dispatch", LIB.ep_dispatch(*self._dispatch_args))
 
     def layout_dispatch(self):
         """layout() and dispatch() as one call (one launch up to 3072 entries)."""
-        check("ep_layout_dispatch", LIB.ep_layout_dispatch(*self._layout_dispatch_args))
+        check("ep_layout_dispatch", self._fn_layout_dispatch(*self._layout_dispatch_args))
 
     def combine(self):
         check("ep_combine", LIB.ep_combine(*self._combine_args))

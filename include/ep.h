@@ -132,6 +132,21 @@ ep_status ep_dispatch_layout_padded(const int32_t* topk_idx, int64_t num_tokens,
                                     size_t workspace_bytes, void* stream);
 
 /*
+ * The same two layout calls with int64 expert ids (the index type routers
+ * usually produce, e.g. a top-k over gate scores): identical results, the
+ * ids read as 64-bit values (8-byte aligned).  An id outside [0, E) is
+ * masked, whatever its width.
+ */
+ep_status ep_dispatch_layout_i64(const int64_t* topk_idx, int64_t num_tokens, int32_t top_k,
+                                 int32_t num_experts, int32_t* tokens_per_expert, int32_t* expert_offset,
+                                 int32_t* slot, int32_t* src_token, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+ep_status ep_dispatch_layout_padded_i64(const int64_t* topk_idx, int64_t num_tokens, int32_t top_k,
+                                        int32_t num_experts, int32_t capacity, int32_t* recv_expert_count,
+                                        int32_t* slot, int32_t* src_token, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
  * ep_dispatch - copy every token into its K receive rows.
  *
  * [P1 "DeepEP 的常规内核和低延迟内核"]: dispatch moves tokens to their
@@ -190,6 +205,14 @@ ep_status ep_layout_dispatch(const int32_t* topk_idx, const void* x, const float
                              int32_t* expert_offset, int32_t* slot, int32_t* src_token, void* recv_x,
                              float* recv_scale, float* recv_weight, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* ep_layout_dispatch with int64 expert ids (8-byte aligned); otherwise identical. */
+ep_status ep_layout_dispatch_i64(const int64_t* topk_idx, const void* x, const float* topk_weights,
+                                 int64_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
+                                 int32_t capacity, int32_t format, int32_t* tokens_per_expert,
+                                 int32_t* expert_offset, int32_t* slot, int32_t* src_token, void* recv_x,
+                                 float* recv_scale, float* recv_weight, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * ep_combine - reduce each token's K expert outputs back to the token.

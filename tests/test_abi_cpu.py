@@ -186,3 +186,22 @@ def test_c_driver_compiles_and_links(lib, tmp_path):
     spec.loader.exec_module(mod)
     r = subprocess.run(mod.command(str(tmp_path / "ep_step")), capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_int64_id_calls_reject_bad_arguments(lib):
+    """The int64-id entry points check what the int32 ones do, with the ids
+    aligned to 8 bytes."""
+    L = lib.LIB.ep_dispatch_layout_i64
+    P = lib.LIB.ep_dispatch_layout_padded_i64
+    F = lib.LIB.ep_layout_dispatch_i64
+    bad = lib.EP_ERR_INVALID_ARG
+    assert L(FAKE + 4, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, None, 0, None) == bad  # 4-byte aligned ids
+    assert L(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, FAKE, None, 0, None) == bad
+    assert L(FAKE, 4, 2, 1025, FAKE, FAKE, FAKE, FAKE, None, 0, None) == lib.EP_ERR_UNSUPPORTED
+    assert P(FAKE + 4, 4, 2, 8, 16, FAKE, FAKE, FAKE, None, 0, None) == bad
+    assert P(FAKE, 4, 2, 8, 0, FAKE, FAKE, FAKE, None, 0, None) == bad
+    fp8 = lib.EP_RECV_FP8_E4M3_G128
+    assert F(FAKE + 4, FAKE, None, 4, 256, 2, 8, 0, fp8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
+             None) == bad
+    assert F(FAKE, FAKE, None, 4, 200, 2, 8, 0, fp8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
+             None) == bad  # H % 128
