@@ -2,13 +2,14 @@
  * ep_step - one MoE step through the C ABI of libep.so, from plain C and the
  * HIP runtime, with no Python (test driver).
  *
- *   ep_step DIR T H K E CAPACITY MODE
+ *   ep_step DIR T H K E CAPACITY MODE [IDS64]
  *
  * Reads DIR/topk_idx.bin (int32 [T,K]), DIR/x.bin (bf16 bits [T,H]),
  * DIR/w.bin (float32 [T,K]) and DIR/y.bin (bf16 bits [rows,H]; rows = T*K,
  * or E*CAPACITY when CAPACITY > 0).  MODE 0 runs the layout call then
  * ep_dispatch; MODE 1 runs ep_layout_dispatch.  Both then run ep_combine.
- * The FP8 receive format is used.  Writes counts.bin, offsets.bin
+ * With IDS64 = 1, topk_idx.bin holds int64 ids and the *_i64 layout calls
+ * are used.  The FP8 receive format is used.  Writes counts.bin, offsets.bin
  * (packed only), slot.bin, src.bin, recv.bin, scale.bin, rweight.bin and
  * out.bin to DIR.  Exits non-zero, with a message, on any error.
  */
@@ -85,10 +86,12 @@ static void* device_buffer(size_t bytes, int fill) {
 }
 
 int main(int argc, char** argv) {
-  if (argc != 8) {
-    fprintf(stderr, "usage: %s DIR T H K E CAPACITY MODE\n", argv[0]);
+  if (argc != 8 && argc != 9) {
+    fprintf(stderr, "usage: %s DIR T H K E CAPACITY MODE [IDS64]\n", argv[0]);
     return 1;
   }
+  const int ids64 = argc == 9 && atoi(argv[8]) == 1;
+  const size_t id_bytes = ids64 ? 8 : 4;
   const char* dir = argv[1];
   const int64_t T = atoll(argv[2]);
   const int32_t H = atoi(argv[3]), K = atoi(argv[4]), E = atoi(argv[5]), cap = atoi(argv[6]);
@@ -96,12 +99,12 @@ int main(int argc, char** argv) {
   const size_t rows = cap > 0 ? (size_t)E * (size_t)cap : (size_t)T * (size_t)K;
   const size_t n = (size_t)T * (size_t)K;
 
-  void* h_idx = read_file(dir, "topk_idx.bin", n * 4);
+  void* h_idx = read_file(dir, "topk_idx.bin", n * id_bytes);
   void* h_x = read_file(dir, "x.bin", (size_t)T * H * 2);
   void* h_w = read_file(dir, "w.bin", n * 4);
   void* h_y = read_file(dir, "y.bin", rows * H * 2);
 
-  int32_t* idx = (int32_t*)upload(h_idx, n * 4);
+  void* idx = upload(h_idx, n * id_bytes);
   void* x = upload(h_x, (size_t)T * H * 2);
   float* w = (float*)upload(h_w, n * 4);
   void* y = upload(h_y, rows * H * 2);
@@ -118,14 +121,22 @@ int main(int argc, char** argv) {
 
   hipStream_t stream;
   HIP_CHECK(hipStreamCreate(&stream));
-  if (mode == 1) {
-    EP_CHECK(ep_layout_dispatch(idx, x, w, T, H, K, E, cap, EP_RECV_FP8_E4M3_G128, counts, offsets, slot, src, recv,
-                                scale, rweight, ws, ws_bytes, stream));
+  if (mode == 1 && ids64) {
+    EP_CHECK(ep_layout_dispatch_i64((const int64_t*)idx, x, w, T, H, K, E, cap, EP_RECV_FP8_E4M3_G128, counts,
+                                    offsets, slot, src, recv, scale, rweight, ws, ws_bytes, stream));
+  } else if (mode == 1) {
+    EP_CHECK(ep_layout_dispatch((const int32_t*)idx, x, w, T, H, K, E, cap, EP_RECV_FP8_E4M3_G128, counts, offsets,
+                                slot, src, recv, scale, rweight, ws, ws_bytes, stream));
   } else {
-    if (cap > 0)
-      EP_CHECK(ep_dispatch_layout_padded(idx, T, K, E, cap, counts, slot, src, ws, ws_bytes, stream));
+    if (cap > 0 && ids64)
+      EP_CHECK(ep_dispatch_layout_padded_i64((const int64_t*)idx, T, K, E, cap, counts, slot, src, ws, ws_bytes,
+                                             stream));
+    else if (cap > 0)
+      EP_CHECK(ep_dispatch_layout_padded((const int32_t*)idx, T, K, E, cap, counts, slot, src, ws, ws_bytes, stream));
+    else if (ids64)
+      EP_CHECK(ep_dispatch_layout_i64((const int64_t*)idx, T, K, E, counts, offsets, slot, src, ws, ws_bytes, stream));
     else
-      EP_CHECK(ep_dispatch_layout(idx, T, K, E, counts, offsets, slot, src, ws, ws_bytes, stream));
+      EP_CHECK(ep_dispatch_layout((const int32_t*)idx, T, K, E, counts, offsets, slot, src, ws, ws_bytes, stream));
     EP_CHECK(ep_dispatch(x, T, H, K, slot, w, EP_RECV_FP8_E4M3_G128, recv, scale, rweight, stream));
   }
   EP_CHECK(ep_combine(y, slot, w, T, H, K, out, stream));
@@ -148,6 +159,7 @@ int main(int argc, char** argv) {
   free(h_x);
   free(h_w);
   free(h_y);
-  printf("ep_step ok: T=%lld H=%d K=%d E=%d capacity=%d mode=%d\n", (long long)T, H, K, E, cap, mode);
+  printf("ep_step ok: T=%lld H=%d K=%d E=%d capacity=%d mode=%d ids64=%d\n", (long long)T, H, K, E, cap, mode,
+         ids64);
   return 0;
 }

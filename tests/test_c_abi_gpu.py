@@ -20,22 +20,24 @@ pytestmark = pytest.mark.gpu
 EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "ep_step")
 
 
+@pytest.mark.parametrize("ids64", [False, True])
 @pytest.mark.parametrize("name,T,cap,mode", [("decode", None, 0, 0), ("decode", None, 0, 1), ("decode", None, 128, 0),
                                              ("decode", None, 128, 1), ("tiny", None, 0, 1), ("tiny", None, 3, 1),
                                              ("prefill", 600, 0, 0), ("prefill", 600, 0, 1)])
-def test_c_driver_matches_oracle(gpu, tmp_path, name, T, cap, mode):
+def test_c_driver_matches_oracle(gpu, tmp_path, name, T, cap, mode, ids64):
+    """ids64: int64 expert ids through the *_i64 entry points."""
     assert os.path.exists(EXE), "C driver not built: run `python tests/c_abi/build.py`"
     wl = make_workload(name, seed=11, T=T)
     T, H, E, K = wl.T, wl.H, wl.E, wl.K
     rows = E * cap if cap else T * K
     rng = np.random.default_rng(11)
     y = to_bf16_bits(rng.standard_normal((rows, H), dtype=np.float32))
-    wl.topk_idx.astype(np.int32).tofile(tmp_path / "topk_idx.bin")
+    wl.topk_idx.astype(np.int64 if ids64 else np.int32).tofile(tmp_path / "topk_idx.bin")
     wl.x_bits.astype(np.uint16).tofile(tmp_path / "x.bin")
     wl.topk_weights.astype(np.float32).tofile(tmp_path / "w.bin")
     y.astype(np.uint16).tofile(tmp_path / "y.bin")
-    print("case c-abi", name, T, cap, mode, flush=True)
-    r = subprocess.run([EXE, str(tmp_path), str(T), str(H), str(K), str(E), str(cap), str(mode)],
+    print("case c-abi", name, T, cap, mode, ids64, flush=True)
+    r = subprocess.run([EXE, str(tmp_path), str(T), str(H), str(K), str(E), str(cap), str(mode), str(int(ids64))],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
 
