@@ -43,6 +43,26 @@ __device__ __forceinline__ int expert_key(Idx e, int E) {
   return (e >= 0 && e < static_cast<Idx>(E)) ? static_cast<int>(e) : E;
 }
 
+// Keys of the 16 / sizeof(Idx) consecutive ids held in one 16-byte load
+// (little-endian: an int64 id is the dword pair lo, hi).
+template <typename Idx>
+__device__ __forceinline__ void expert_keys16(const int4 v, int E, int* key) {
+  if constexpr (sizeof(Idx) == 4) {
+    key[0] = expert_key(v.x, E);
+    key[1] = expert_key(v.y, E);
+    key[2] = expert_key(v.z, E);
+    key[3] = expert_key(v.w, E);
+  } else {
+    static_assert(sizeof(Idx) == 8, "ids are int32 or int64");
+    const auto join = [](int lo, int hi) {
+      return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                  static_cast<uint32_t>(lo));
+    };
+    key[0] = expert_key(join(v.x, v.y), E);
+    key[1] = expert_key(join(v.z, v.w), E);
+  }
+}
+
 // Inclusive prefix sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
   const int lane = threadIdx.x & (kWave - 1);

@@ -42,7 +42,7 @@ namespace {
 constexpr int kSingleMaxWaves = 8;  // the single-workgroup path launches at most 8 waves
 constexpr int kSingleMaxThreads = kSingleMaxWaves * 64;
 constexpr int kSingleMaxEntries = 1024;  // one workgroup, no workspace
-constexpr int kFusedMaxEntries = 65536;   // one launch, no workspace
+constexpr int kOneLaunchMaxEntries = 65536;  // one launch, no workspace
 constexpr int kMultiThreads = 256;
 constexpr int kMultiWaves = kMultiThreads / kWave;
 
@@ -277,7 +277,10 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
 // scan of the totals, and an entry's row is offset + before + (own-chunk
 // rank).  Every block reads all T*K ids (from L2 after the first), which
 // trades redundant on-chip work for the second launch and the workspace.
-// V4: 16-byte id loads (int32 ids aligned to 16 bytes only).
+// All blocks walk the ids in the same order: one L2 miss per XCD then serves
+// every block on it (a per-block rotated start measured 1.7x slower with
+// int64 ids).
+// V4: 16-byte id loads (ids aligned to 16 bytes): 4 int32 or 2 int64 ids each.
 template <int NW, bool V4, typename Idx>
 __global__ __launch_bounds__(NW * kWave) void layout_fused(
     const Idx* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t* __restrict__ counts,
@@ -309,11 +312,11 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
     atomicAdd(p < c0 ? &before[k] : &after[k], 1);
   };
   if constexpr (V4) {
-    static_assert(sizeof(Idx) == 4, "16-byte id loads read int32 ids");
-    // 16-byte loads: 4 ids each, 8 loads in flight per thread
+    // 16-byte loads of kPer ids each, 32 ids in flight per thread
+    constexpr int kPer = 16 / static_cast<int>(sizeof(Idx));
+    constexpr int kUnroll = 32 / kPer;
     const int4* idx4 = reinterpret_cast<const int4*>(idx);
-    const int n4 = R / 4;
-    constexpr int kUnroll = 8;
+    const int n4 = R / kPer;
     for (int q0 = 0; q0 < n4; q0 += kThreads * kUnroll) {
       int4 e[kUnroll];
 #pragma unroll
@@ -325,13 +328,13 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
       for (int u = 0; u < kUnroll; ++u) {
         const int q = q0 + u * kThreads + tid;
         if (q >= n4) continue;
-        count_one(4 * q, expert_key(e[u].x, E));
-        count_one(4 * q + 1, expert_key(e[u].y, E));
-        count_one(4 * q + 2, expert_key(e[u].z, E));
-        count_one(4 * q + 3, expert_key(e[u].w, E));
+        int k4[kPer];
+        expert_keys16<Idx>(e[u], E, k4);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) count_one(kPer * q + j, k4[j]);
       }
     }
-    const int p = 4 * n4 + tid;  // the last R % 4 ids
+    const int p = kPer * n4 + tid;  // the last R % kPer ids
     if (p < R) count_one(p, expert_key(idx[p], E));
   } else {
     constexpr int kUnroll = 16;
@@ -403,7 +406,7 @@ enum class LayoutPath { kSingle, kFused, kMulti };
 
 LayoutPath choose_path(int64_t rows) {
   if (rows <= kSingleMaxEntries) return LayoutPath::kSingle;
-  if (rows <= kFusedMaxEntries) return LayoutPath::kFused;
+  if (rows <= kOneLaunchMaxEntries) return LayoutPath::kFused;
   return LayoutPath::kMulti;
 }
 
@@ -444,17 +447,13 @@ hipError_t launch_layout(const Idx* topk_idx, int32_t rows, int32_t top_k, int32
     const int chunk = nw * kWave;
     const dim3 grid((rows + chunk - 1) / chunk), block(chunk);
     const size_t lds = fused_lds_bytes(nw, E);
-    // 16-byte id loads: int32 ids aligned to 16 bytes
-    const bool v4 = sizeof(Idx) == 4 && (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0;
+    // 16-byte id loads: ids aligned to 16 bytes
+    const bool v4 = (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0;
 #define EP_LAYOUT_FUSED_V(NW, V)                                                                                  \
   hipLaunchKernelGGL((layout_fused<NW, V, Idx>), grid, block, lds, stream, topk_idx, rows, top_k, E, capacity, \
                      counts, offsets, slot, src)
-#define EP_LAYOUT_FUSED(NW)                                                   \
-  if constexpr (sizeof(Idx) == 4) {                                           \
-    if (v4) EP_LAYOUT_FUSED_V(NW, true); else EP_LAYOUT_FUSED_V(NW, false);    \
-  } else {                                                                    \
-    EP_LAYOUT_FUSED_V(NW, false);                                             \
-  }
+#define EP_LAYOUT_FUSED(NW) \
+  if (v4) EP_LAYOUT_FUSED_V(NW, true); else EP_LAYOUT_FUSED_V(NW, false)
     if (nw >= 16) { EP_LAYOUT_FUSED(16); }
     else if (nw >= 8) { EP_LAYOUT_FUSED(8); }
     else if (nw >= 4) { EP_LAYOUT_FUSED(4); }

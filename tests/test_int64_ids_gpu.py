@@ -130,3 +130,31 @@ def test_conveniences_and_plan_keep_int64(gpu):
             plan.step()
         assert np.array_equal(host(plan.slot), oslot)
         assert np.array_equal(host(plan.out.view(torch.int16)), oracle.combine(y, oslot, wl.topk_weights))
+
+
+@pytest.mark.parametrize("T,K,misalign", [(4096, 8, False), (4096, 8, True), (1001, 3, False), (1001, 3, True),
+                                          (8191, 8, False)])
+def test_one_launch_layout_id_loads(gpu, T, K, misalign):
+    """The one-launch layout reads int64 ids two per 16-byte load when the ids
+    are 16-byte aligned (odd T*K leaves a last id for the scalar tail), and
+    one per load when they sit 8 bytes past a 16-byte boundary."""
+    ep = gpu
+    E = 256
+    rng = np.random.default_rng(7 * T + K + misalign)
+    idx = wide_ids(rng, T, K, E)
+    print("case int64 one-launch layout T=%d K=%d misalign=%d" % (T, K, misalign), flush=True)
+    n = T * K
+    store = torch.empty(n + 2, dtype=torch.int64, device="cuda")
+    d_idx = store[1:n + 1] if misalign else store[:n]
+    d_idx.copy_(torch.from_numpy(idx.ravel()))
+    d_idx = d_idx.view(T, K)
+    assert (d_idx.data_ptr() % 16 == 8) == misalign
+    counts = torch.full((E,), SENT_I32, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), SENT_I32, dtype=torch.int32, device="cuda")
+    slot = torch.full((T, K), SENT_I32, dtype=torch.int32, device="cuda")
+    src = torch.full((n,), SENT_I32, dtype=torch.int32, device="cuda")
+    assert ep.ep_layout_workspace_bytes(T, K, E) == 0
+    ep.ep_dispatch_layout(d_idx, E, counts, offsets, slot, src, None)
+    oc, oo, oslot, osrc = oracle.dispatch_layout(idx, E)
+    assert np.array_equal(host(counts), oc) and np.array_equal(host(offsets), oo)
+    assert np.array_equal(host(slot), oslot) and np.array_equal(host(src), osrc)
