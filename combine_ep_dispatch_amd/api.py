@@ -61,6 +61,9 @@ def _need(t, name, dtypes, shape=None):
 
 _I32 = (torch.int32,)
 _IDX = (torch.int32, torch.int64)  # expert ids: int32, or int64 as routers produce them
+_F32 = (torch.float32,)
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8, torch.float8_e4m3fn)
 
 
 def _ids_fn(name, topk_idx):
@@ -74,9 +77,6 @@ def _as_ids(topk_idx):
     if topk_idx.dtype not in _IDX:
         topk_idx = topk_idx.to(torch.int32)
     return topk_idx.contiguous()
-_F32 = (torch.float32,)
-_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
-_U8 = (torch.uint8, torch.float8_e4m3fn)
 
 
 def ep_layout_workspace_bytes(num_tokens, top_k, num_experts):
@@ -359,7 +359,7 @@ def dispatch(x, topk_idx, topk_weights, num_experts, fp8=True, handle=None, stre
 def combine(y, handle, topk_weights, stream=None):
     """Weighted reduction of expert outputs ``y`` [T*K, H] (bf16, receive
     order) back to token order -> bfloat16 [T, H]."""
-    T, K = handle.slot.shape
+    T = handle.slot.shape[0]
     out = torch.empty((T, y.shape[1]), dtype=torch.bfloat16, device=y.device)
     ep_combine(y, handle.slot, topk_weights.to(torch.float32).contiguous(), out, stream)
     return out
@@ -427,7 +427,7 @@ def low_latency_combine(y, handle, topk_weights, stream=None):
 
 def dispatch_backward(grad_recv, handle, stream=None):
     """Gradient of dispatch w.r.t. x: the K copies' gradients summed -> bf16 [T, H]."""
-    T, K = handle.slot.shape
+    T = handle.slot.shape[0]
     R = grad_recv.shape[0]
     out = torch.empty((T, grad_recv.shape[1]), dtype=torch.bfloat16, device=grad_recv.device)
     ep_dispatch_backward(grad_recv, handle.slot, out, stream, num_rows=R)

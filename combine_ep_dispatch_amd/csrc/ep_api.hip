@@ -17,6 +17,15 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // second pass (at most 1024 chunks of 4096 entries).
 constexpr int64_t kMaxRows = int64_t(1) << 22;
 
+// Largest T*H handled by dispatch, combine and their backward: their
+// kernels launch T*H/16 or T*H/8 work items (the per-token backward
+// workgroups at most T*(H/8 + 63)).  Below 2^31 items the 32-bit item
+// counts and grid arithmetic are exact and every launch is in range.
+constexpr int64_t kMaxElems = int64_t(1) << 34;
+
+// Largest n handled by ep_cast_fp8_e4m3 (n/4 work items, below 2^31).
+constexpr int64_t kMaxCast = int64_t(1) << 33;
+
 ep_status from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
 
 ep_status check_common(int64_t T, int32_t K) {
@@ -66,7 +75,7 @@ ep_status check_dispatch(const void* x, int64_t T, int32_t H, int32_t K, const f
   if (format == EP_RECV_FP8_E4M3_G128 && H % 128 != 0) return EP_ERR_INVALID_ARG;
   if (H % 8 != 0) return EP_ERR_INVALID_ARG;
   if (recv_weight != nullptr && topk_weights == nullptr) return EP_ERR_INVALID_ARG;
-  if (T * H >= (int64_t(1) << 35)) return EP_ERR_UNSUPPORTED;
+  if (T * H >= kMaxElems) return EP_ERR_UNSUPPORTED;
   if (T == 0) return EP_OK;
   if (!x || !recv_x) return EP_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(recv_x, 16)) return EP_ERR_INVALID_ARG;
@@ -223,7 +232,7 @@ EP_API ep_status ep_combine(const void* y, const int32_t* slot, const float* top
   ep_status st = check_common(num_tokens, top_k);
   if (st != EP_OK) return st;
   if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARG;
-  if (num_tokens * hidden >= (int64_t(1) << 35)) return EP_ERR_UNSUPPORTED;
+  if (num_tokens * hidden >= kMaxElems) return EP_ERR_UNSUPPORTED;
   if (num_tokens == 0) return EP_OK;
   if (!y || !slot || !topk_weights || !out) return EP_ERR_INVALID_ARG;
   if (!aligned(y, 16) || !aligned(out, 16) || !aligned(slot, 4) || !aligned(topk_weights, 4))
@@ -238,7 +247,7 @@ EP_API ep_status ep_dispatch_backward(const void* grad_recv, const int32_t* slot
   ep_status st = check_common(num_tokens, top_k);
   if (st != EP_OK) return st;
   if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARG;
-  if (num_tokens * hidden >= (int64_t(1) << 35)) return EP_ERR_UNSUPPORTED;
+  if (num_tokens * hidden >= kMaxElems) return EP_ERR_UNSUPPORTED;
   if (num_tokens == 0) return EP_OK;
   if (!grad_recv || !slot || !grad_x) return EP_ERR_INVALID_ARG;
   if (!aligned(grad_recv, 16) || !aligned(grad_x, 16) || !aligned(slot, 4)) return EP_ERR_INVALID_ARG;
@@ -254,6 +263,7 @@ EP_API ep_status ep_combine_backward(const void* grad_out, const void* y, const 
   if (st != EP_OK) return st;
   if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARG;
   if (hidden > 8192) return EP_ERR_UNSUPPORTED;
+  if (num_tokens * hidden >= kMaxElems) return EP_ERR_UNSUPPORTED;
   if (num_tokens == 0) return EP_OK;
   if (!grad_out || !slot || !topk_weights || !grad_y) return EP_ERR_INVALID_ARG;
   if (grad_w != nullptr && y == nullptr) return EP_ERR_INVALID_ARG;
@@ -268,7 +278,7 @@ EP_API ep_status ep_combine_backward(const void* grad_out, const void* y, const 
 
 EP_API ep_status ep_cast_fp8_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
   if (n < 0) return EP_ERR_INVALID_ARG;
-  if (n >= (int64_t(1) << 40)) return EP_ERR_UNSUPPORTED;
+  if (n >= kMaxCast) return EP_ERR_UNSUPPORTED;
   if (n == 0) return EP_OK;
   if (!in || !out || !aligned(in, 16) || !aligned(out, 16)) return EP_ERR_INVALID_ARG;
   return from_hip(ep::launch_cast_fp8(in, out, n, static_cast<hipStream_t>(stream)));

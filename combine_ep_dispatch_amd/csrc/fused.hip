@@ -18,9 +18,10 @@
 // Encoding an entry as key*n + p turns either count into one integer range
 // test per entry: the packed row counts codes below the entry's own, the
 // padded rank the codes from key*n up to it (entries with a code below
-// key*n are exactly those of a smaller key).  Each wavefront compares 64 entries per step against its token's
-// K codes and counts the matches with a ballot and a popcount, so the
-// counts stay wave-uniform and only the four per-wave totals meet, in LDS.
+// key*n are exactly those of a smaller key).  Each wavefront compares 64
+// entries per step against its token's K codes and counts the matches with
+// a ballot and a popcount, so the counts stay wave-uniform and only the
+// per-wave totals meet, in LDS.
 // Integer counting is exact and order-free: the result is a pure function
 // of topk_idx.
 //

@@ -53,7 +53,7 @@ class StepPlan:
         self.counts = torch.empty(E, dtype=torch.int32, device=dev)
         self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
         self.slot = torch.empty((T, K), dtype=torch.int32, device=dev)
-        self.src = torch.empty(rows if self.capacity else T * K, dtype=torch.int32, device=dev)
+        self.src = torch.empty(rows, dtype=torch.int32, device=dev)
         nb = api.ep_layout_workspace_bytes(T, K, E)
         self.workspace = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
         self.fmt = EP_RECV_FP8_E4M3_G128 if fp8 else EP_RECV_BF16

@@ -66,8 +66,9 @@ typedef enum {
 const char* ep_status_string(int status);
 
 /* Bytes of device workspace ep_dispatch_layout, ep_dispatch_layout_padded
- * and ep_layout_dispatch need for this shape: 0 up to 65536 entries (T*K), which one launch
- * handles; beyond, (E+1) int32 per 4096-entry chunk.  Pure host function. */
+ * and ep_layout_dispatch (and their _i64 forms) need for this shape: 0 up
+ * to 65536 entries (T*K), which one launch handles; beyond, (E+1) int32
+ * per 4096-entry chunk.  Pure host function. */
 size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t top_k, int32_t num_experts);
 
 /*
@@ -171,7 +172,7 @@ ep_status ep_dispatch_layout_padded_i64(const int64_t* topk_idx, int64_t num_tok
  * recv_weight  float32 [rows] out or NULL
  * Rows no entry maps to are left untouched.  Requirements: H > 0,
  * H % 128 == 0 for FP8, H % 8 == 0 for BF16, 1 <= K <= EP_MAX_TOPK,
- * T*K <= 2^22, T*H < 2^35.
+ * T*K <= 2^22, T*H < 2^34.
  */
 ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, int32_t top_k,
                       const int32_t* slot, const float* topk_weights, int32_t format,
@@ -279,7 +280,7 @@ ep_status ep_combine_backward(const void* grad_out, const void* y, const int32_t
  * beyond 448 saturate to +-448; NaN inputs are outside the contract.
  * Exposed so the conversion can be checked exhaustively against its
  * definition (OCP 8-bit floating point specification v1.0).
- * in float32 [n], out uint8 [n]; n >= 0; both 16-byte aligned.
+ * in float32 [n], out uint8 [n]; 0 <= n < 2^33; both 16-byte aligned.
  */
 ep_status ep_cast_fp8_e4m3(const float* in, uint8_t* out, int64_t n, void* stream);
 

@@ -103,6 +103,23 @@ def test_dispatch_and_combine_reject_bad_arguments(lib):
     assert lib.LIB.ep_cast_fp8_e4m3(None, None, 0, None) == lib.EP_OK
 
 
+def test_size_limits_keep_launches_in_range(lib):
+    """T*H reaches 2**34 (2**21 tokens of hidden 8192, top-1): every call that
+    launches T*H/8 or T*H/16 work items refuses it, as the FP8 cast refuses
+    n = 2**33, so no launch reaches 2**31 work items."""
+    L, U = lib.LIB, lib.EP_ERR_UNSUPPORTED
+    T, H, fp8 = 1 << 21, 8192, lib.EP_RECV_FP8_E4M3_G128
+    assert L.ep_dispatch(FAKE, T, H, 1, FAKE, None, fp8, FAKE, FAKE, None, None) == U
+    assert L.ep_dispatch(FAKE, T, H, 1, FAKE, None, lib.EP_RECV_BF16, FAKE, None, None, None) == U
+    assert L.ep_combine(FAKE, FAKE, FAKE, T, H, 1, FAKE, None) == U
+    assert L.ep_dispatch_backward(FAKE, FAKE, T, H, 1, FAKE, None) == U
+    assert L.ep_combine_backward(FAKE, FAKE, FAKE, FAKE, T, H, 1, FAKE, None, None) == U
+    ws = lib.ep_layout_workspace_bytes(T, 1, 8)
+    assert L.ep_layout_dispatch(FAKE, FAKE, None, T, H, 1, 8, 0, fp8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                FAKE, ws, None) == U
+    assert L.ep_cast_fp8_e4m3(FAKE, FAKE, 1 << 33, None) == U
+
+
 def test_product_package_does_not_import_the_oracle():
     pkg = os.path.join(ROOT, "combine_ep_dispatch_amd")
     for dirpath, _, files in os.walk(pkg):
