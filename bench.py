@@ -14,8 +14,8 @@ are seeded synthetic tensors already resident in HBM when timing starts.
 
 The JSON line reports throughput as algorithmic bytes per second (bytes the
 method must move, every one of the K copies counted), the per-kernel
-launch durations measured with HIP events on the launch stream, the
-roofline of the dominant kernel (combine), p10 / median / p90 of single
+launch durations (K back-to-back launches of each kernel between two HIP
+events on the launch stream), the roofline of the dominant kernel (combine), p10 / median / p90 of single
 steps warm and with the Infinity Cache flushed before each, the decode-size (128 tokens)
 step time (eager launches through the checked binding and through
 StepPlan, and as a replayed HIP graph, packed and with the low-latency
@@ -133,6 +133,15 @@ class Setup:
         self.dispatch()
         self.combine()
 
+    def bare(self):
+        """A StepPlan on the same inputs: the same kernels, launched through
+        pre-built C calls, so back-to-back launches of a short kernel are
+        not paced by the host."""
+        if getattr(self, "_plan", None) is None:
+            self._plan = self.ep.StepPlan(self.idx, self.w, self.x, self.wl.E, capacity=self.capacity,
+                                          fp8=self.wl.fp8, y=self.y)
+        return self._plan
+
     def layout_dispatch(self):
         # one call for layout + dispatch (one launch up to 3072 entries)
         self.ep.ep_layout_dispatch(self.idx, self.x, None, self.wl.E, self.capacity, self.fmt, self.counts,
@@ -161,8 +170,11 @@ class Setup:
 
 def time_steps(torch, s, steps, warmup):
     """K steps bracketed by synchronisation, timed with HIP events on the
-    stream the kernels are launched on; then the same K steps again with an
-    event between consecutive calls for the per-kernel durations."""
+    stream the kernels are launched on; then, for each of the three calls,
+    K back-to-back launches of it (bare C calls on the same inputs) between
+    two events: its mean launch duration, the kernel plus one launch gap.
+    An event recorded between every two calls would add ~5 µs to each
+    interval on MI355X."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         s.step()
@@ -176,23 +188,11 @@ def time_steps(torch, s, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     us_step = a.elapsed_time(b) * 1e3 / steps
-
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    for m in marks:
-        m[0].record(stream)
-        s.layout()
-        m[1].record(stream)
-        s.dispatch()
-        m[2].record(stream)
-        s.combine()
-        m[3].record(stream)
-    torch.cuda.synchronize()
-    per = {"layout": [], "dispatch": [], "combine": []}
-    for m in marks:
-        per["layout"].append(m[0].elapsed_time(m[1]) * 1e3)
-        per["dispatch"].append(m[1].elapsed_time(m[2]) * 1e3)
-        per["combine"].append(m[2].elapsed_time(m[3]) * 1e3)
-    return us_step, {k: sum(v) / len(v) for k, v in per.items()}, wall
+    plan = s.bare()
+    plan.layout()
+    per = {name: time_loop(torch, fn, steps, 1)
+           for name, fn in (("layout", plan.layout), ("dispatch", plan.dispatch), ("combine", plan.combine))}
+    return us_step, per, wall
 
 
 def time_distribution(torch, s, reps, flush_bytes=0):
@@ -270,21 +270,6 @@ def time_graph(torch, step, replays):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e3 / replays
-
-
-def time_calls(torch, fn, reps, warmup=3):
-    """Mean µs of one call, HIP events around each call on the launch stream."""
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in ev:
-        a.record(stream)
-        fn()
-        b.record(stream)
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) * 1e3 / reps
 
 
 def read_traffic():
@@ -377,6 +362,7 @@ rocprofv3 --kernel-trace --stats -d OUT/prof_trace -o trace --output-format csv 
 rocprofv3 --pmc FETCH_SIZE -d OUT/prof_fetch -o fetch --output-format csv -- python3 bench.py --profile-pass
 rocprofv3 --pmc WRITE_SIZE -d OUT/prof_write -o write --output-format csv -- python3 bench.py --profile-pass
 rocprofv3 --kernel-trace --stats -d OUT/prof_decode -o decode --output-format csv -- python3 bench.py --profile-pass decode
+rocprofv3 --kernel-trace --stats -d OUT/prof_bench -o bench --output-format csv -- python3 bench.py > OUT/bench_under_rocprof.json
 python3 bench.py --summarize-profile OUT
 """
 
@@ -476,10 +462,53 @@ def summarize_profile(dirname):
               "only while it matches)"]
     with open(TRAFFIC_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
-    for p in ("prefill_4096x7168_top8_kernel_trace.txt", "decode_128x7168_top8_kernel_trace.txt",
-              os.path.basename(TRAFFIC_FILE)):
+    written = ["prefill_4096x7168_top8_kernel_trace.txt", "decode_128x7168_top8_kernel_trace.txt",
+               os.path.basename(TRAFFIC_FILE)]
+    if summarize_bench_run(dirname, rows, short):
+        written.append(BENCH_RUN_FILE)
+    for p in written:
         if os.path.exists(os.path.join(PROFILES, p)):
             print(open(os.path.join(PROFILES, p)).read())
+
+
+BENCH_RUN_FILE = "prefill_4096x7168_top8_bench_run.txt"
+
+
+def summarize_bench_run(dirname, rows, short):
+    """The default bench command run under rocprofv3 --kernel-trace: the
+    profiler's mean duration of each prefill step kernel over all its
+    launches in that process, beside the HIP-event durations (kernel_us)
+    that the same process printed in its JSON line."""
+    stats = {short(r["Name"]): r for r in rows("prof_bench", "*kernel_stats.csv")}
+    path = os.path.join(dirname, "bench_under_rocprof.json")
+    if not stats or not os.path.exists(path):
+        return False
+    rec = None
+    for line in open(path):
+        if line.startswith("{"):
+            rec = json.loads(line)
+    if rec is None:
+        return False
+    lines = ["The default bench command under rocprofv3 --kernel-trace --stats: the profiler's mean",
+             "duration of each prefill step kernel over all its launches in the process (the timed steps,",
+             "the per-kernel and single-step timings, warm and flushed), beside kernel_us, the means over",
+             "K back-to-back launches that the same process printed (HIP events on the launch stream).",
+             "Under the tracer every launch costs several microseconds more, which inflates the back-to-back",
+             "figure of a kernel as short as the layout (and the decode-size timings of that run); the",
+             "prefill dispatch and combine are long enough not to notice.", "", "commands:", PROFILE_COMMANDS,
+             "%-34s %6s %14s %14s %8s" % ("kernel", "calls", "rocprof_avg_us", "bench_us", "ratio")]
+    for step, kern in STEP_KERNELS.items():
+        r = stats.get(kern)
+        if r is None:
+            continue
+        prof_us = float(r["AverageNs"]) / 1e3
+        bench_us = rec["kernel_us"][step]
+        lines.append("%-34s %6s %14.2f %14.2f %8.3f" % (kern, r["Calls"], prof_us, bench_us, bench_us / prof_us))
+    lines += ["", "bench line of that run: value %s %s, us_per_step %s, roofline %s"
+              % (rec["value"], rec["unit"], rec["us_per_step"], json.dumps(rec["roofline"]))]
+    with open(os.path.join(PROFILES, BENCH_RUN_FILE), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return True
 
 
 def other_workload(ep, torch, args):
@@ -555,8 +584,8 @@ def main():
     dist = {"warm": time_distribution(torch, s, 50), "flushed": time_distribution(torch, s, 50, 512 << 20)}
     s.backward_buffers(torch)
     db_b, cb_b = backward_bytes(s.wl.T, s.wl.H, s.wl.K)
-    db_us = time_calls(torch, s.dispatch_backward, 30)
-    cb_us = time_calls(torch, s.combine_backward, 30)
+    db_us = time_loop(torch, s.dispatch_backward, 30, 3)
+    cb_us = time_loop(torch, s.combine_backward, 30, 3)
 
     # decode: three calls (layout, dispatch, combine), then the fused form
     # (layout + dispatch in one launch, then combine), each eager through
@@ -568,11 +597,11 @@ def main():
         d_us, d_per, _ = time_steps(torch, d, 200, 10)
         rec_d = {"stream": round(d_us, 2), "graph": round(time_graph(torch, d.step, args.decode_replays), 2),
                  "kernel_us": {k: round(v, 2) for k, v in d_per.items()}}
-        plan = ep.StepPlan(d.idx, d.w, d.x, d.wl.E, capacity=cap, y=d.y)
+        plan = d.bare()
         rec_d["fused"] = {"stream": round(time_loop(torch, d.step_fused, 200, 10), 2),
                           "stream_step_plan": round(time_loop(torch, plan.step, 200, 10), 2),
                           "graph": round(time_graph(torch, d.step_fused, args.decode_replays), 2),
-                          "kernel_us": {"layout_dispatch": round(time_calls(torch, d.layout_dispatch, 200), 2)}}
+                          "kernel_us": {"layout_dispatch": round(time_loop(torch, plan.layout_dispatch, 200, 10), 2)}}
         decode[cap] = rec_d
         del d, plan
 
@@ -598,6 +627,8 @@ def main():
         "us_per_step": round(us_step, 2),
         "us_per_step_graph": round(graph_us, 2),
         "kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
+        "kernel_us_method": "mean of K back-to-back launches of each kernel, HIP events on the launch stream "
+                            "(kernel plus one launch gap)",
         "kernel_alg_bytes": {"layout": lay_b, "dispatch": dis_b, "combine": com_b},
         "step_distribution_us": dict(dist, note="50 steps each timed alone (events between the calls); flushed: "
                                                 "a 512 MB device read before every step evicts the Infinity Cache"),
