@@ -381,7 +381,9 @@ size_t fused_lds_bytes(int nw, int E) {
   return nw * nk * 12 + 2 * nk * 4 + nw * 4;
 }
 
-constexpr size_t kLdsLimit = 65536;
+// LDS one workgroup may allocate on gfx950: the CU's whole 160 KB.  Up to
+// 512 experts the one-launch layout keeps 16 waves; at 1024, 8.
+constexpr size_t kLdsLimit = 160 * 1024;
 
 size_t single_lds_bytes(int nw, int E) {
   const size_t nk = static_cast<size_t>(E) + 1;

@@ -100,7 +100,8 @@ def test_expert_counts(gpu, E):
 
 @pytest.mark.parametrize("rows,E", [(1024, 256), (1025, 256), (4095, 256), (32767, 256), (32768, 256),
                                     (65536, 256), (65537, 256), (131073, 256), (262144, 256),
-                                    (1024, 1024), (1025, 1024), (65536, 1024), (65537, 1024), (700, 1),
+                                    (1024, 512), (1025, 512), (32768, 512), (65536, 512),
+                                    (1024, 1024), (1025, 1024), (32768, 1024), (65536, 1024), (65537, 1024), (700, 1),
                                     (5000, 1)])
 def test_layout_path_boundaries(gpu, rows, E):
     """One workgroup up to 1024 entries, one fused launch up to 65536, then

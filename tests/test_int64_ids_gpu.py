@@ -43,7 +43,8 @@ def run_layout(ep, idx64, E, cap):
 
 
 @pytest.mark.parametrize("T,K,E,cap", [(64, 8, 256, 0), (128, 8, 256, 0), (1000, 8, 256, 0), (9000, 8, 256, 0),
-                                       (128, 8, 256, 16), (9000, 8, 256, 40), (300, 3, 1024, 0)])
+                                       (128, 8, 256, 16), (9000, 8, 256, 40), (300, 3, 1024, 0),
+                                       (4096, 8, 1024, 0), (4096, 8, 512, 64)])
 def test_layout_paths(gpu, T, K, E, cap):
     ep = gpu
     rng = np.random.default_rng(T + K + E + cap)
