@@ -133,3 +133,59 @@ def test_two_streams_at_once(gpu):
         orecv, oscale, _ = oracle.dispatch_fp8(wl.x_bits, oslot)
         assert np.array_equal(host(plan.recv_x)[:nv], orecv[:nv])
         assert np.array_equal(host(plan.out.view(torch.int16)), oracle.combine(y, oslot, wl.topk_weights))
+
+
+def test_host_threads_at_once(gpu):
+    """Four host threads step four plans at the same time, each on its own
+    stream (ctypes releases the interpreter lock during every C call, so the
+    library really is entered concurrently): packed, padded, a batch whose
+    layout takes two launches through a workspace, and a tiny one.  Each
+    plan's outputs match the oracle."""
+    import threading
+
+    ep = gpu
+    # (workload, tokens, hidden, capacity); 9000 x 8 entries take the two-launch layout
+    cases = [("decode", None, None, 0), ("decode", None, None, 64), ("skew", 9000, 256, 0), ("tiny", None, None, 0)]
+    plans, ys, wls = [], [], []
+    print("case host threads", flush=True)
+    for i, (name, T, H, cap) in enumerate(cases):
+        wl = make_workload(name, seed=40 + i, T=T, **({"H": H} if H else {}))
+        idx = torch.from_numpy(wl.topk_idx).cuda()
+        w = torch.from_numpy(wl.topk_weights).cuda()
+        x = torch.from_numpy(wl.x_bits.view(np.int16)).cuda()
+        plan = ep.StepPlan(idx, w, x, wl.E, capacity=cap, stream=torch.cuda.Stream())
+        y = to_bf16_bits(np.random.default_rng(40 + i).standard_normal((plan.rows, wl.H), dtype=np.float32))
+        plan.y.copy_(torch.from_numpy(y.view(np.int16)).cuda().view(torch.bfloat16))
+        plans.append(plan)
+        ys.append(y)
+        wls.append(wl)
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(plan):
+        try:
+            for _ in range(25):
+                plan.step()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(p,)) for p in plans]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for plan, y, wl, (name, T, H, cap) in zip(plans, ys, wls, cases):
+        if cap:
+            oc, oslot, osrc = oracle.dispatch_layout_padded(wl.topk_idx, wl.E, cap)
+            valid = (oslot.ravel() >= 0)
+            rows = np.unique(oslot.ravel()[valid])
+        else:
+            oc, oo, oslot, osrc = oracle.dispatch_layout(wl.topk_idx, wl.E)
+            rows = np.arange(int(oo[-1]))
+        assert np.array_equal(host(plan.counts), oc) and np.array_equal(host(plan.slot), oslot)
+        orecv, oscale, _ = oracle.dispatch_fp8(wl.x_bits, oslot, num_rows=plan.rows)
+        assert np.array_equal(host(plan.recv_x)[rows], orecv[rows])
+        assert np.array_equal(host(plan.recv_scale)[rows].view(np.uint32), oscale[rows].view(np.uint32))
+        assert np.array_equal(host(plan.out.view(torch.int16)), oracle.combine(y, oslot, wl.topk_weights))
