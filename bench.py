@@ -253,13 +253,15 @@ def time_loop(torch, fn, steps, warmup):
     return a.elapsed_time(b) * 1e3 / steps
 
 
-def time_graph(torch, step, replays):
-    """`step` captured once in a HIP graph and replayed; returns µs per step."""
+def time_graph(torch, step, replays, steps_per_graph=1):
+    """`step` captured `steps_per_graph` times in one HIP graph and replayed;
+    returns µs per step (events on the stream the graph is launched on)."""
     step()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        step()
+        for _ in range(steps_per_graph):
+            step()
     for _ in range(5):
         g.replay()
     torch.cuda.synchronize()
@@ -269,7 +271,7 @@ def time_graph(torch, step, replays):
         g.replay()
     b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / replays
+    return a.elapsed_time(b) * 1e3 / (replays * steps_per_graph)
 
 
 def read_traffic():
@@ -601,6 +603,9 @@ def main():
         rec_d["fused"] = {"stream": round(time_loop(torch, d.step_fused, 200, 10), 2),
                           "stream_step_plan": round(time_loop(torch, plan.step, 200, 10), 2),
                           "graph": round(time_graph(torch, d.step_fused, args.decode_replays), 2),
+                          # one graph launch costs more host time than this step's GPU time;
+                          # ten steps in one graph amortise it
+                          "graph_10_steps": round(time_graph(torch, d.step_fused, args.decode_replays // 10, 10), 2),
                           "kernel_us": {"layout_dispatch": round(time_loop(torch, plan.layout_dispatch, 200, 10), 2)}}
         decode[cap] = rec_d
         del d, plan
