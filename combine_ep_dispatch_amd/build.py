@@ -8,7 +8,8 @@ libep.so, which is what this script produces.)
 Each .hip file is compiled to an object in parallel, then linked.  The
 library links against the HIP runtime that torch loads (torch/lib), so a
 process that uses torch for device memory and streams and this library for
-the kernels holds one HIP runtime, not two.
+the kernels holds one HIP runtime, not two.  Without torch it links
+$ROCM_PATH/lib's runtime; EP_HIP_LIB_DIR picks another directory.
 """
 
 import concurrent.futures as cf
@@ -40,13 +41,21 @@ FLAGS = [
 ]
 
 
-def _torch_lib_dir():
+def _hip_lib_dir():
+    """Directory of the libamdhip64 to link: $EP_HIP_LIB_DIR if set; else
+    the one torch loads (torch/lib), so that a process using torch for
+    memory and streams holds a single HIP runtime; else $ROCM_PATH/lib (a
+    build for plain C callers on a machine without torch)."""
     import importlib.util
 
+    if os.environ.get("EP_HIP_LIB_DIR"):
+        return os.environ["EP_HIP_LIB_DIR"]
     spec = importlib.util.find_spec("torch")
-    if spec is None or not spec.submodule_search_locations:
-        raise RuntimeError("torch is required to locate the HIP runtime it loads")
-    return os.path.join(list(spec.submodule_search_locations)[0], "lib")
+    if spec is not None and spec.submodule_search_locations:
+        tl = os.path.join(list(spec.submodule_search_locations)[0], "lib")
+        if os.path.exists(os.path.join(tl, "libamdhip64.so")):
+            return tl
+    return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
 
 
 def _run(cmd):
@@ -67,7 +76,7 @@ def build(verbose=False):
         for log in ex.map(_run, jobs):
             if verbose and log.strip():
                 print(log)
-    tl = _torch_lib_dir()
+    tl = _hip_lib_dir()
     tmp = OUT + ".tmp"
     log = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-L" + tl, "-Wl,-rpath," + tl,
                 "-lamdhip64", "-o", tmp])
