@@ -17,7 +17,7 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 
-def test_algorithmic_bytes_match_the_survey_table():
+def test_algorithmic_bytes_match_the_tabulated_totals():
     """Totals per configuration as tabulated from the byte formulas when the
     workloads were specified (MB = 1e6 bytes, three significant decimals)."""
     def mb(v):

@@ -14,7 +14,7 @@ Trained router statistics are not available, so gate logits are N(0, 1).
 """
 
 from .gen import (  # noqa: F401
-    CONFIGS,
+    WORKLOADS,
     Workload,
     make_workload,
     make_x_bits,

@@ -102,7 +102,7 @@ def route_zipf(rng, T, E, k, s=1.2, holes_frac=0.0):
     return idx.astype(np.int32), w.astype(np.float32)
 
 
-CONFIGS = {
+WORKLOADS = {
     "tiny": dict(T=64, H=256, E=16, K=2, routing="softmax", fp8=True),
     "decode": dict(T=128, H=7168, E=256, K=8, routing="group", fp8=True),
     "prefill": dict(T=4096, H=7168, E=256, K=8, routing="group", fp8=True),
@@ -154,7 +154,7 @@ class Workload:
 
 
 def make_routing(name, seed, T=None, **over):
-    cfg = dict(CONFIGS[name])
+    cfg = dict(WORKLOADS[name])
     cfg.update(over)
     if T is not None:
         cfg["T"] = T
@@ -172,7 +172,7 @@ def make_routing(name, seed, T=None, **over):
 
 
 def make_workload(name, seed=0, T=None, **over):
-    """Build the seeded workload ``name`` (a key of CONFIGS).
+    """Build the seeded workload ``name`` (a key of WORKLOADS).
 
     ``T`` overrides the token count (same routing recipe); other keyword
     overrides replace config fields (e.g. ``holes_frac=0.25`` for the
