@@ -26,8 +26,8 @@
 // Three launch shapes, chosen by T*K:
 //  * up to 1024 entries: `layout_single`, one workgroup does everything;
 //  * up to 65536: `layout_fused`, one launch of 1024-entry chunks in which
-//    every workgroup also histograms all entries outside its chunk, so no
-//    cross-workgroup exchange (and no workspace) is needed;
+//    every workgroup also histograms all entries, so no cross-workgroup
+//    exchange (and no workspace) is needed;
 //  * beyond: `layout_count` ranks 4096-entry chunks and writes per-chunk
 //    histograms to the workspace, then `layout_finalize` sums the
 //    histograms of earlier chunks per key (16 loads in flight per thread),
@@ -45,6 +45,7 @@ constexpr int kSingleMaxEntries = 1024;  // one workgroup, no workspace
 constexpr int kOneLaunchMaxEntries = 65536;  // one launch, no workspace
 constexpr int kMultiThreads = 256;
 constexpr int kMultiWaves = kMultiThreads / kWave;
+constexpr int kHistCopies = 4;  // one-launch layout: private histograms per lane & 3
 
 // Rank ITERS consecutive 64-entry steps of this wavefront: entries
 // [p_begin, p_end).  lmask (E+1 lane masks, all zero on entry and on exit)
@@ -270,16 +271,21 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
 
 // One launch for the whole layout.  Block b owns the chunk of NW*64
 // consecutive entries starting at b*NW*64 (one 64-entry step per wave) and
-// ranks it as above; it also histograms every entry outside its chunk with
-// LDS atomic adds (integer addition is order-free, so the counts are exact
-// and deterministic), split into entries before and after the chunk.  Then
-// for every key: total = before + own + after, offsets are the exclusive
-// scan of the totals, and an entry's row is offset + before + (own-chunk
-// rank).  Every block reads all T*K ids (from L2 after the first), which
-// trades redundant on-chip work for the second launch and the workspace.
-// All blocks walk the ids in the same order: one L2 miss per XCD then serves
-// every block on it (a per-block rotated start measured 1.7x slower with
-// int64 ids).
+// ranks it as above; it also histograms all T*K entries with LDS atomic
+// adds (integer addition is order-free, so the counts are exact and
+// deterministic): entries before its chunk into `before`, the rest, its
+// chunk included, into `after`.  Then for every key: total = before +
+// after, offsets are the exclusive scan of the totals, and an entry's row
+// is offset + before + (own-chunk rank).  Every block reads all T*K ids
+// (from L2 after the first), which trades redundant on-chip work for the
+// second launch and the workspace.  The histogram step is issue-bound (16
+// waves on 4 SIMDs, every instruction paid once per entry), so it spends
+// one LDS atomic and its address per entry: which histogram takes a load's
+// ids is one block-uniform comparison per 16-byte load, and lanes spread
+// over kHistCopies private copies so that a hot expert's entries in one
+// wave collide on fewer addresses.  All blocks walk the ids in the same
+// order: one L2 miss per XCD then serves every block on it (a per-block
+// rotated start measured 1.7x slower with int64 ids).
 // V4: 16-byte id loads (ids aligned to 16 bytes): 4 int32 or 2 int64 ids each.
 template <int NW, bool V4, typename Idx>
 __global__ __launch_bounds__(NW * kWave) void layout_fused(
@@ -291,14 +297,14 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
   const int nk = E + 1;
   uint64_t* lmask = lds64;                             // [NW][nk]
   int* cnt = reinterpret_cast<int*>(lmask + NW * nk);  // [NW][nk]
-  int* before = cnt + NW * nk;                         // [nk]
-  int* after = before + nk;                            // [nk], later totals and offsets
-  int* wave_tot = after + nk;                          // [NW]
+  int* before = cnt + NW * nk;                         // [kHistCopies][nk], merged into copy 0
+  int* after = before + kHistCopies * nk;              // [kHistCopies][nk], copy 0 later totals and offsets
+  int* wave_tot = after + kHistCopies * nk;            // [NW]
   for (int i = tid; i < NW * nk; i += kThreads) {
     lmask[i] = 0;
     cnt[i] = 0;
   }
-  for (int i = tid; i < nk; i += kThreads) {
+  for (int i = tid; i < kHistCopies * nk; i += kThreads) {
     before[i] = 0;
     after[i] = 0;
   }
@@ -306,17 +312,22 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
 
   const int c0 = blockIdx.x * kThreads;
   const int c1 = min(R, c0 + kThreads);
-  // count entry p (outside this block's chunk) into the before/after histogram
-  auto count_one = [&](int p, int k) {
-    if (p >= c0 && p < c1) return;
-    atomicAdd(p < c0 ? &before[k] : &after[k], 1);
-  };
+  // Histogram every entry: those before this block's chunk into `before`,
+  // the rest (the chunk itself included) into `after`, so the per-key total
+  // is before + after.  Lanes spread over kHistCopies private copies, so
+  // entries of one hot expert in one wave collide on fewer LDS addresses.
+  const int copy = (lane & (kHistCopies - 1)) * nk;
+  int* const hb = before + copy;
+  int* const ha = after + copy;
   if constexpr (V4) {
-    // 16-byte loads of kPer ids each, 32 ids in flight per thread
+    // 16-byte loads of kPer ids each, 32 ids in flight per thread.  c0 is
+    // a multiple of the chunk size and so of kPer: each load lies wholly
+    // before or wholly at/after c0 (one block-uniform comparison per load),
+    // and the last R % kPer ids all lie at or after c0
     constexpr int kPer = 16 / static_cast<int>(sizeof(Idx));
     constexpr int kUnroll = 32 / kPer;
     const int4* idx4 = reinterpret_cast<const int4*>(idx);
-    const int n4 = R / kPer;
+    const int n4 = R / kPer, qb = c0 / kPer;
     for (int q0 = 0; q0 < n4; q0 += kThreads * kUnroll) {
       int4 e[kUnroll];
 #pragma unroll
@@ -328,14 +339,15 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
       for (int u = 0; u < kUnroll; ++u) {
         const int q = q0 + u * kThreads + tid;
         if (q >= n4) continue;
+        int* const h = q < qb ? hb : ha;
         int k4[kPer];
         expert_keys16<Idx>(e[u], E, k4);
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) count_one(kPer * q + j, k4[j]);
+        for (int j = 0; j < kPer; ++j) atomicAdd(&h[k4[j]], 1);
       }
     }
     const int p = kPer * n4 + tid;  // the last R % kPer ids
-    if (p < R) count_one(p, expert_key(idx[p], E));
+    if (p < R) atomicAdd(&ha[expert_key(idx[p], E)], 1);
   } else {
     constexpr int kUnroll = 16;
     for (int q0 = 0; q0 < R; q0 += kThreads * kUnroll) {
@@ -348,7 +360,7 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int p = q0 + u * kThreads + tid;
-        if (p < R) count_one(p, e[u]);
+        if (p < R) atomicAdd(&(p < c0 ? hb : ha)[e[u]], 1);
       }
     }
   }
@@ -366,7 +378,14 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
       cnt[ww * nk + j] = run;
       run += c;
     }
-    after[j] = before[j] + run + after[j];  // total
+    int b = 0, a = 0;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) {
+      b += before[c * nk + j];
+      a += after[c * nk + j];
+    }
+    before[j] = b;
+    after[j] = b + a;  // total: `after` counted this block's chunk too
   }
   __syncthreads();
   block_exclusive_scan(after, nk, wave_tot);
@@ -378,7 +397,7 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
 
 size_t fused_lds_bytes(int nw, int E) {
   const size_t nk = static_cast<size_t>(E) + 1;
-  return nw * nk * 12 + 2 * nk * 4 + nw * 4;
+  return nw * nk * 12 + 2 * kHistCopies * nk * 4 + nw * 4;
 }
 
 // LDS one workgroup may allocate on gfx950: the CU's whole 160 KB.  Up to
