@@ -63,42 +63,54 @@ __device__ __forceinline__ void expert_keys16(const int4 v, int E, int* key) {
   }
 }
 
-// Inclusive prefix sum over the 64 lanes of a wavefront.
+// Inclusive prefix sum over the 64 lanes of a wavefront, with DPP: shifts
+// by 1, 2, 4 and 8 inside each 16-lane row (lanes without a source add 0),
+// then row_bcast:15 adds row 0's total to row 1 and row 2's to row 3, and
+// row_bcast:31 adds the total of rows 0-1 to rows 2 and 3.  Integer
+// addition, so the order of the partial sums does not matter.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
   return x;
 }
 
-// Exclusive prefix sum of data[0..n) in LDS, in place.  Every thread of the
-// block must call it.  wave_tot needs blockDim.x / 64 ints of LDS.
-__device__ inline void block_exclusive_scan(int* data, int n, int* wave_tot) {
-  const int tid = threadIdx.x, bs = blockDim.x;
-  const int lane = tid & (kWave - 1), w = tid / kWave, nw = bs / kWave;
-  const int per = (n + bs - 1) / bs;
-  const int beg = min(n, tid * per), end = min(n, beg + per);
-  int local = 0;
-  for (int i = beg; i < end; ++i) local += data[i];
-  const int incl = wave_inclusive_scan(local);
-  if (lane == kWave - 1) wave_tot[w] = incl;
-  __syncthreads();
-  if (w == 0) {
-    const int v = lane < nw ? wave_tot[lane] : 0;
-    const int s = wave_inclusive_scan(v);
-    if (lane < nw) wave_tot[lane] = s - v;
+// Exclusive prefix sum of data[0..n) in LDS, in place, by wave 0 alone:
+// each lane sums ceil(n/64) consecutive values, the lanes' sums are scanned
+// across the wave, and each lane rewrites its run.  Every thread of the
+// block must call it (it ends with the barrier that publishes the result).
+// MAXPER bounds ceil(n/64): the lane's values stay in registers.
+template <int MAXPER>
+__device__ inline void block_exclusive_scan_upto(int* data, int n) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int per = (n + kWave - 1) / kWave;
+    const int beg = lane * per;
+    int v[MAXPER];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      v[i] = (i < per && beg + i < n) ? data[beg + i] : 0;
+      local += v[i];
+    }
+    int run = wave_inclusive_scan(local) - local;
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      if (i < per && beg + i < n) data[beg + i] = run;
+      run += v[i];
+    }
   }
   __syncthreads();
-  int run = wave_tot[w] + incl - local;
-  for (int i = beg; i < end; ++i) {
-    const int c = data[i];
-    data[i] = run;
-    run += c;
-  }
-  __syncthreads();
+}
+
+// n <= 17 * 64 (up to 1024 experts and the masked key)
+__device__ inline void block_exclusive_scan(int* data, int n) {
+  if (n <= 5 * kWave) block_exclusive_scan_upto<5>(data, n);
+  else if (n <= 9 * kWave) block_exclusive_scan_upto<9>(data, n);
+  else block_exclusive_scan_upto<17>(data, n);
 }
 
 // ---- number formats -------------------------------------------------------

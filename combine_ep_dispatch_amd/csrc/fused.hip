@@ -53,10 +53,10 @@ constexpr int kMaxWaves = kMaxThreads / kWave;
 constexpr int kMaxK = 32;
 static_assert(static_cast<int64_t>(1025) * kFusedMaxEntries < (int64_t(1) << 31), "entry codes fit int32");
 
-// LDS: workgroup 0 needs E+1 histogram bins and the scan's wave totals; the
-// token workgroups need the per-wave counts, the K rows and the K keys.
+// LDS: workgroup 0 needs E+1 histogram bins; the token workgroups need the
+// per-wave counts, the K rows and the K keys.
 constexpr int kTokenLdsInts = kMaxWaves * kMaxK + 2 * kMaxK;
-constexpr int kLdsInts = 1025 + kMaxWaves > kTokenLdsInts ? 1025 + kMaxWaves : kTokenLdsInts;
+constexpr int kLdsInts = 1025 > kTokenLdsInts ? 1025 : kTokenLdsInts;
 
 // This lane's keys: entries u*blockDim + tid for u < NS, with the address
 // clamped to the last entry (n >= 1) so that all NS loads are issued back
@@ -84,7 +84,6 @@ __device__ void write_counts_block(const Idx* __restrict__ idx, int n, int E, in
                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
   const int tid = threadIdx.x, bs = blockDim.x, nk = E + 1;
   int* hist = lds;
-  int* wave_tot = lds + nk;
   int e[NS];  // keys
   if (n > 0) load_keys<NS>(idx, n, E, e);  // block-uniform; nothing to read for an empty batch
   for (int i = tid; i < nk; i += bs) hist[i] = 0;
@@ -97,7 +96,7 @@ __device__ void write_counts_block(const Idx* __restrict__ idx, int n, int E, in
   __syncthreads();
   for (int j = tid; j < E; j += bs) counts[j] = cap == 0 ? hist[j] : min(hist[j], cap);
   if (cap == 0) {  // block-uniform
-    block_exclusive_scan(hist, nk, wave_tot);
+    block_exclusive_scan(hist, nk);
     for (int j = tid; j <= E; j += bs) offsets[j] = hist[j];
   }
 }

@@ -59,17 +59,23 @@ constexpr int kHistCopies = 4;  // one-launch layout: private histograms per lan
 // those lanes below this one plus the running count; the lowest such lane
 // advances the count and clears the mask.  LDS operations of one wavefront
 // execute in program order, which is all the step relies on.
+// load_wave_keys reads the keys (the ranking below takes them preloaded,
+// so a caller can issue the loads early).
 template <int ITERS, typename Idx>
-__device__ __forceinline__ void rank_wave_range(const Idx* __restrict__ idx, int p_begin, int p_end,
-                                                int E, uint64_t* lmask, int* cnt, int (&key)[ITERS],
-                                                int (&rank)[ITERS]) {
+__device__ __forceinline__ void load_wave_keys(const Idx* __restrict__ idx, int p_begin, int p_end, int E,
+                                               int (&e)[ITERS]) {
   const int lane = threadIdx.x & (kWave - 1);
-  int e[ITERS];  // keys
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
     const int p = p_begin + i * kWave + lane;
     e[i] = p < p_end ? expert_key(idx[p], E) : E;
   }
+}
+
+template <int ITERS>
+__device__ __forceinline__ void rank_wave_keys(const int (&e)[ITERS], int p_begin, int p_end, uint64_t* lmask,
+                                               int* cnt, int (&key)[ITERS], int (&rank)[ITERS]) {
+  const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
     if (p_begin + i * kWave >= p_end) {  // wave-uniform: nothing left
@@ -94,6 +100,15 @@ __device__ __forceinline__ void rank_wave_range(const Idx* __restrict__ idx, int
     key[i] = inr ? k : -1;
     rank[i] = pre + below;
   }
+}
+
+template <int ITERS, typename Idx>
+__device__ __forceinline__ void rank_wave_range(const Idx* __restrict__ idx, int p_begin, int p_end,
+                                                int E, uint64_t* lmask, int* cnt, int (&key)[ITERS],
+                                                int (&rank)[ITERS]) {
+  int e[ITERS];
+  load_wave_keys<ITERS>(idx, p_begin, p_end, E, e);
+  rank_wave_keys<ITERS>(e, p_begin, p_end, lmask, cnt, key, rank);
 }
 
 // Row of one entry whose rank among the entries of its key is `within`.
@@ -142,7 +157,6 @@ __global__ __launch_bounds__(kSingleMaxThreads) void layout_single(
   uint64_t* lmask = lds64;                                // [nw][nk]
   int* cnt = reinterpret_cast<int*>(lmask + nw * nk);     // [nw][nk]
   int* off = cnt + nw * nk;                               // [nk]
-  int* wave_tot = off + nk;                               // [nw]
   for (int i = tid; i < nw * nk; i += bs) {
     lmask[i] = 0;
     cnt[i] = 0;
@@ -166,7 +180,7 @@ __global__ __launch_bounds__(kSingleMaxThreads) void layout_single(
     off[j] = run;
   }
   __syncthreads();
-  block_exclusive_scan(off, nk, wave_tot);
+  block_exclusive_scan(off, nk);
   write_counts(off, E, cap, 0, counts, offsets);
 
   const int lane = tid & (kWave - 1);
@@ -227,7 +241,6 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
   const int nk = E + 1;
   int* base = lds;            // [nk] rows of this key in earlier chunks
   int* off = lds + nk;        // [nk] totals, then offsets
-  int* wave_tot = off + nk;   // [kMultiWaves]
   const int b = blockIdx.x;
   constexpr int kChunk = kMultiThreads * ITERS;
 
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
     off[j] = total;
   }
   __syncthreads();
-  block_exclusive_scan(off, nk, wave_tot);
+  block_exclusive_scan(off, nk);
   write_counts(off, E, cap, b, counts, offsets);
 
 #pragma unroll
@@ -299,16 +312,17 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
   int* cnt = reinterpret_cast<int*>(lmask + NW * nk);  // [NW][nk]
   int* before = cnt + NW * nk;                         // [kHistCopies][nk], merged into copy 0
   int* after = before + kHistCopies * nk;              // [kHistCopies][nk], copy 0 later totals and offsets
-  int* wave_tot = after + kHistCopies * nk;            // [NW]
-  for (int i = tid; i < NW * nk; i += kThreads) {
-    lmask[i] = 0;
-    cnt[i] = 0;
-  }
-  for (int i = tid; i < kHistCopies * nk; i += kThreads) {
-    before[i] = 0;
-    after[i] = 0;
-  }
-  __syncthreads();
+  // clear the lane masks, running counts and histograms (callers sync)
+  auto clear_lds = [&]() {
+    for (int i = tid; i < NW * nk; i += kThreads) {
+      lmask[i] = 0;
+      cnt[i] = 0;
+    }
+    for (int i = tid; i < kHistCopies * nk; i += kThreads) {
+      before[i] = 0;
+      after[i] = 0;
+    }
+  };
 
   const int c0 = blockIdx.x * kThreads;
   const int c1 = min(R, c0 + kThreads);
@@ -316,6 +330,10 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
   // the rest (the chunk itself included) into `after`, so the per-key total
   // is before + after.  Lanes spread over kHistCopies private copies, so
   // entries of one hot expert in one wave collide on fewer LDS addresses.
+  // this wave's 64 entries of the chunk, ranked after the histogram; their
+  // keys are loaded with the first batch of ids
+  const int p_begin = c0 + w * kWave, p_stop = min(c1, p_begin + kWave);
+  int own[1];
   const int copy = (lane & (kHistCopies - 1)) * nk;
   int* const hb = before + copy;
   int* const ha = after + copy;
@@ -328,13 +346,24 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
     constexpr int kUnroll = 32 / kPer;
     const int4* idx4 = reinterpret_cast<const int4*>(idx);
     const int n4 = R / kPer, qb = c0 / kPer;
-    for (int q0 = 0; q0 < n4; q0 += kThreads * kUnroll) {
-      int4 e[kUnroll];
+    int4 e[kUnroll];
+    auto load_batch = [&](int q0) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int q = q0 + u * kThreads + tid;
         e[u] = q < n4 ? idx4[q] : make_int4(0, 0, 0, 0);
       }
+    };
+    // the first batch is loaded before the LDS is cleared, so the loads'
+    // latency overlaps the clearing and the waves' start (at 32768 int32 or
+    // int64 ids one batch is all of them); the empty asm keeps the compiler
+    // from sinking the loads below the clearing
+    load_batch(0);
+    load_wave_keys<1>(idx, p_begin, p_stop, E, own);
+    asm volatile("" ::: "memory");
+    clear_lds();
+    __syncthreads();
+    for (int q0 = 0;;) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int q = q0 + u * kThreads + tid;
@@ -345,10 +374,16 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
 #pragma unroll
         for (int j = 0; j < kPer; ++j) atomicAdd(&h[k4[j]], 1);
       }
+      q0 += kThreads * kUnroll;
+      if (q0 >= n4) break;
+      load_batch(q0);
     }
     const int p = kPer * n4 + tid;  // the last R % kPer ids
     if (p < R) atomicAdd(&ha[expert_key(idx[p], E)], 1);
   } else {
+    load_wave_keys<1>(idx, p_begin, p_stop, E, own);
+    clear_lds();
+    __syncthreads();
     constexpr int kUnroll = 16;
     for (int q0 = 0; q0 < R; q0 += kThreads * kUnroll) {
       int e[kUnroll];  // keys
@@ -366,8 +401,7 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
   }
 
   int key[1], rank[1];
-  const int p_begin = c0 + w * kWave;
-  rank_wave_range<1>(idx, p_begin, min(c1, p_begin + kWave), E, lmask + w * nk, cnt + w * nk, key, rank);
+  rank_wave_keys<1>(own, p_begin, p_stop, lmask + w * nk, cnt + w * nk, key, rank);
   __syncthreads();
 
   for (int j = tid; j < nk; j += kThreads) {
@@ -388,7 +422,7 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
     after[j] = b + a;  // total: `after` counted this block's chunk too
   }
   __syncthreads();
-  block_exclusive_scan(after, nk, wave_tot);
+  block_exclusive_scan(after, nk);
   write_counts(after, E, cap, blockIdx.x, counts, offsets);
 
   const int k = key[0];
@@ -397,7 +431,7 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
 
 size_t fused_lds_bytes(int nw, int E) {
   const size_t nk = static_cast<size_t>(E) + 1;
-  return nw * nk * 12 + 2 * kHistCopies * nk * 4 + nw * 4;
+  return nw * nk * 12 + 2 * kHistCopies * nk * 4;
 }
 
 // LDS one workgroup may allocate on gfx950: the CU's whole 160 KB.  Up to
@@ -406,7 +440,7 @@ constexpr size_t kLdsLimit = 160 * 1024;
 
 size_t single_lds_bytes(int nw, int E) {
   const size_t nk = static_cast<size_t>(E) + 1;
-  return nw * nk * 8 + nw * nk * 4 + nk * 4 + nw * 4;
+  return nw * nk * 8 + nw * nk * 4 + nk * 4;
 }
 
 int single_waves(int E) {
@@ -487,7 +521,7 @@ hipError_t launch_layout(const Idx* topk_idx, int32_t rows, int32_t top_k, int32
   const int nblocks = (rows + chunk - 1) / chunk;
   int32_t* hist = static_cast<int32_t*>(workspace);
   const size_t lds_count = static_cast<size_t>(kMultiWaves * nk) * (sizeof(uint64_t) + sizeof(int));
-  const size_t lds_final = static_cast<size_t>(2 * nk + kMultiWaves) * sizeof(int);
+  const size_t lds_final = static_cast<size_t>(2 * nk) * sizeof(int);
   const dim3 grid(nblocks), block(kMultiThreads);
   hipLaunchKernelGGL((layout_count<kMultiIters, Idx>), grid, block, lds_count, stream, topk_idx, rows, E, slot,
                      hist);
