@@ -124,10 +124,11 @@ __device__ __forceinline__ void count_targets(const int (&te)[KC], int p0, int k
   }
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
-    if (u >= nsteps) break;  // wave-uniform
+    if (u < nsteps) {  // wave-uniform
 #pragma unroll
-    for (int j = 0; j < KC; ++j)
-      c[j] += __popcll(wave_ballot(static_cast<uint32_t>(code[u] - lo[j]) < static_cast<uint32_t>(span[j])));
+      for (int j = 0; j < KC; ++j)
+        c[j] += __popcll(wave_ballot(static_cast<uint32_t>(code[u] - lo[j]) < static_cast<uint32_t>(span[j])));
+    }
   }
   const int w = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) {
