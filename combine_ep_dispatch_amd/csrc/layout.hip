@@ -25,9 +25,9 @@
 //
 // Three launch shapes, chosen by T*K:
 //  * up to 1024 entries: `layout_single`, one workgroup does everything;
-//  * up to 65536: `layout_fused`, one launch of 1024-entry chunks in which
-//    every workgroup also histograms all entries, so no cross-workgroup
-//    exchange (and no workspace) is needed;
+//  * up to 65536: `layout_fused`, one launch of 1024-entry chunks (512
+//    with 1024 experts) in which every workgroup also histograms all
+//    entries, so no cross-workgroup exchange (and no workspace) is needed;
 //  * beyond: `layout_count` ranks 4096-entry chunks and writes per-chunk
 //    histograms to the workspace, then `layout_finalize` sums the
 //    histograms of earlier chunks per key (16 loads in flight per thread),
@@ -47,20 +47,9 @@ constexpr int kMultiThreads = 256;
 constexpr int kMultiWaves = kMultiThreads / kWave;
 constexpr int kHistCopies = 4;  // one-launch layout: private histograms per lane & 3
 
-// Rank ITERS consecutive 64-entry steps of this wavefront: entries
-// [p_begin, p_end).  lmask (E+1 lane masks, all zero on entry and on exit)
-// and cnt (E+1 running counts) are this wave's LDS rows.  On return key[i]
-// is the entry's key (E for masked, -1 past p_end) and rank[i] its position
-// among the wave's entries with that key.
-//
-// Per step every in-range lane ORs its lane bit into lmask[key]; reading
-// lmask[key] back gives the set of lanes holding the same key (OR is
-// order-free, so the result is deterministic).  The rank is the number of
-// those lanes below this one plus the running count; the lowest such lane
-// advances the count and clears the mask.  LDS operations of one wavefront
-// execute in program order, which is all the step relies on.
-// load_wave_keys reads the keys (the ranking below takes them preloaded,
-// so a caller can issue the loads early).
+// The keys of this wavefront's entries p_begin + 64*i + lane (E past
+// p_end), loaded apart from the ranking so that a caller can issue the
+// loads early.
 template <int ITERS, typename Idx>
 __device__ __forceinline__ void load_wave_keys(const Idx* __restrict__ idx, int p_begin, int p_end, int E,
                                                int (&e)[ITERS]) {
@@ -72,6 +61,19 @@ __device__ __forceinline__ void load_wave_keys(const Idx* __restrict__ idx, int 
   }
 }
 
+// Rank ITERS consecutive 64-entry steps of this wavefront: entries
+// [p_begin, p_end) with keys e (from load_wave_keys).  lmask (E+1 lane
+// masks, all zero on entry and on exit) and cnt (E+1 running counts) are
+// this wave's LDS rows.  On return key[i] is the entry's key (E for masked,
+// -1 past p_end) and rank[i] its position among the wave's entries with
+// that key.
+//
+// Per step every in-range lane ORs its lane bit into lmask[key]; reading
+// lmask[key] back gives the set of lanes holding the same key (OR is
+// order-free, so the result is deterministic).  The rank is the number of
+// those lanes below this one plus the running count; the lowest such lane
+// advances the count and clears the mask.  LDS operations of one wavefront
+// execute in program order, which is all the step relies on.
 template <int ITERS>
 __device__ __forceinline__ void rank_wave_keys(const int (&e)[ITERS], int p_begin, int p_end, uint64_t* lmask,
                                                int* cnt, int (&key)[ITERS], int (&rank)[ITERS]) {
@@ -102,6 +104,7 @@ __device__ __forceinline__ void rank_wave_keys(const int (&e)[ITERS], int p_begi
   }
 }
 
+// load_wave_keys then rank_wave_keys
 template <int ITERS, typename Idx>
 __device__ __forceinline__ void rank_wave_range(const Idx* __restrict__ idx, int p_begin, int p_end,
                                                 int E, uint64_t* lmask, int* cnt, int (&key)[ITERS],
@@ -291,12 +294,12 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
 // after, offsets are the exclusive scan of the totals, and an entry's row
 // is offset + before + (own-chunk rank).  Every block reads all T*K ids
 // (from L2 after the first), which trades redundant on-chip work for the
-// second launch and the workspace.  The histogram step is issue-bound (16
-// waves on 4 SIMDs, every instruction paid once per entry), so it spends
-// one LDS atomic and its address per entry: which histogram takes a load's
-// ids is one block-uniform comparison per 16-byte load, and lanes spread
-// over kHistCopies private copies so that a hot expert's entries in one
-// wave collide on fewer addresses.  All blocks walk the ids in the same
+// second launch and the workspace.  Everything in the histogram step is
+// paid once per entry (32 per lane at 32768 entries), so it spends one LDS
+// atomic and its address per entry: which histogram takes a load's ids is
+// one block-uniform comparison per 16-byte load, and lanes spread over
+// kHistCopies private copies so that a hot expert's entries in one wave
+// collide on fewer addresses.  All blocks walk the ids in the same
 // order: one L2 miss per XCD then serves every block on it (a per-block
 // rotated start measured 1.7x slower with int64 ids).
 // V4: 16-byte id loads (ids aligned to 16 bytes): 4 int32 or 2 int64 ids each.
@@ -414,9 +417,9 @@ __global__ __launch_bounds__(NW * kWave) void layout_fused(
     }
     int b = 0, a = 0;
 #pragma unroll
-    for (int c = 0; c < kHistCopies; ++c) {
-      b += before[c * nk + j];
-      a += after[c * nk + j];
+    for (int cp = 0; cp < kHistCopies; ++cp) {
+      b += before[cp * nk + j];
+      a += after[cp * nk + j];
     }
     before[j] = b;
     after[j] = b + a;  // total: `after` counted this block's chunk too
