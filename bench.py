@@ -42,7 +42,7 @@ KERNEL_SOURCES = sorted("combine_ep_dispatch_amd/csrc/" + f for f in os.listdir(
                         if f.endswith((".hip", ".h")))
 TRAFFIC_FILE = os.path.join(PROFILES, "prefill_4096x7168_top8_counter_traffic.txt")
 # the prefill step's kernels as they appear in the profile
-STEP_KERNELS = {"layout": "layout_fused<16, true, int>", "dispatch": "dispatch_fp8_kernel<8, true>",
+STEP_KERNELS = {"layout": "layout_fused<16, true, int>", "dispatch": "dispatch_fp8_kernel<8, true, true>",
                 "combine": "combine_kernel<8, false, true>"}
 
 

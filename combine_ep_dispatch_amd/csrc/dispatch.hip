@@ -39,19 +39,56 @@ __device__ __forceinline__ u32x4 load_token(const u32x4* p) {
 }
 
 // Receive rows (and weights) of entries k0 .. k0+KC-1 of one token, loaded
-// together before any store so their latencies overlap.
+// together before any store so their latencies overlap.  The row loads
+// have no per-lane condition, and the weights are loaded by every lane of
+// a wave that needs them (load_w is wave-uniform; wrow is then valid): a
+// load under a per-lane branch makes the compiler wait for each load
+// before issuing the next.
 template <int KC>
 __device__ __forceinline__ void load_rows(const int32_t* __restrict__ srow, const float* __restrict__ wrow,
-                                          int k0, int K, bool want_w, int32_t (&r)[KC], float (&wk)[KC]) {
+                                          int k0, int K, bool load_w, int32_t (&r)[KC], float (&wk)[KC]) {
 #pragma unroll
-  for (int j = 0; j < KC; ++j) {
-    const bool in = k0 + j < K;
-    r[j] = in ? srow[k0 + j] : -1;
-    wk[j] = (in && want_w) ? wrow[k0 + j] : 0.0f;
+  for (int j = 0; j < KC; ++j) r[j] = k0 + j < K ? srow[k0 + j] : -1;
+#pragma unroll
+  for (int j = 0; j < KC; ++j) wk[j] = 0.0f;
+  if (load_w) {
+#pragma unroll
+    for (int j = 0; j < KC; ++j) wk[j] = k0 + j < K ? wrow[k0 + j] : 0.0f;
   }
 }
 
-template <int KT, bool NT>
+// The 8 group scales one wavefront covers, written 32 bytes per row: lanes
+// 0, 8, .., 56 hold them (after quantize16_e4m3), and lane j < KC writes
+// all 8 to its row rj, the token's j-th (loaded by that lane itself: a
+// select among the lanes' copies would be turned into an indexed array
+// in LDS).  For a wave that lies inside one token, with 16-byte-aligned
+// 32-byte pieces (checked at launch).
+template <int KC, bool NT>
+__device__ __forceinline__ void store_wave_scales(int32_t rj, float s, uint32_t v, uint32_t G,
+                                                  float* __restrict__ recv_scale) {
+  const int lane = threadIdx.x & (kWave - 1);
+  u32x4 lo, hi;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = __builtin_amdgcn_readlane(__float_as_uint(s), 8 * i);
+    hi[i] = __builtin_amdgcn_readlane(__float_as_uint(s), 8 * (i + 4));
+  }
+  if (lane < KC && rj >= 0) {
+    u32x4* dst = reinterpret_cast<u32x4*>(recv_scale + static_cast<size_t>(rj) * G + ((v - lane) >> 3));
+    if (NT) {
+      __builtin_nontemporal_store(lo, dst);
+      __builtin_nontemporal_store(hi, dst + 1);
+    } else {
+      dst[0] = lo;
+      dst[1] = hi;
+    }
+  }
+}
+
+// WS: every wavefront lies inside one token (H/16 a multiple of 64) and
+// recv_scale takes 16-byte stores, so the scales go out 32 bytes per row
+// (store_wave_scales); otherwise one lane per group stores its scale.
+template <int KT, bool NT, bool WS>
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const uint16_t* __restrict__ x, uint32_t n_items, uint32_t vpt, int32_t H, int32_t Krt,
     const int32_t* __restrict__ slot, const float* __restrict__ w, uint8_t* __restrict__ recv,
@@ -66,22 +103,24 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
   const float* wrow = w != nullptr ? w + static_cast<size_t>(t) * K : nullptr;
   const bool want_w = recv_weight != nullptr && v == 0;
 
-  // issue the receive-row loads first; they overlap the token load and the
-  // quantisation below
-  int32_t r[KC];
-  float wk[KC];
-  if (active) load_rows<KC>(srow, wrow, 0, K, want_w, r, wk);
-
+  // the token's loads first, then the receive rows: all are in flight
+  // before anything waits for one of them
   u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
   if (active) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * H) + 2 * v;
     a = load_token<NT>(src);
     b = load_token<NT>(src + 1);
   }
+  int32_t r[KC];
+  float wk[KC];
+  if (active) load_rows<KC>(srow, wrow, 0, K, recv_weight != nullptr, r, wk);
+  const int lane = threadIdx.x & (kWave - 1);
+  int32_t rj = -1;  // WS: this lane's row for the scale stores
+  if (WS && active && lane < KC && lane < K) rj = srow[lane];
   float s;
   const u32x4 q = quantize16_e4m3(a, b, s);
 
-  if (!active) return;
+  if (!active) return;  // with WS whole wavefronts only
   const uint32_t G = static_cast<uint32_t>(H) / kGroup;
   const bool lead = (v & 7) == 0;  // one lane per group writes the scale
   for (int k0 = 0;;) {
@@ -89,12 +128,17 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     for (int j = 0; j < KC; ++j) {
       if (r[j] < 0) continue;
       reinterpret_cast<u32x4*>(recv + static_cast<size_t>(r[j]) * H)[v] = q;
-      if (lead) recv_scale[static_cast<size_t>(r[j]) * G + (v >> 3)] = s;
+      if (!WS && lead) {
+        float* ps = recv_scale + static_cast<size_t>(r[j]) * G + (v >> 3);
+        if (NT) __builtin_nontemporal_store(s, ps); else *ps = s;
+      }
       if (want_w) recv_weight[r[j]] = wk[j];
     }
+    if (WS) store_wave_scales<KC, NT>(rj, s, v, G, recv_scale);
     k0 += KC;
     if (k0 >= K) break;
-    load_rows<KC>(srow, wrow, k0, K, want_w, r, wk);
+    load_rows<KC>(srow, wrow, k0, K, recv_weight != nullptr, r, wk);
+    if (WS) rj = lane < KC && k0 + lane < K ? srow[k0 + lane] : -1;
   }
 }
 
@@ -112,10 +156,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
   const int32_t* srow = slot + static_cast<size_t>(t) * K;
   const float* wrow = w != nullptr ? w + static_cast<size_t>(t) * K : nullptr;
   const bool want_w = recv_weight != nullptr && v == 0;
+  const u32x4 d = load_token<NT>(reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * H) + v);
   int32_t r[KC];
   float wk[KC];
-  load_rows<KC>(srow, wrow, 0, K, want_w, r, wk);
-  const u32x4 d = load_token<NT>(reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * H) + v);
+  load_rows<KC>(srow, wrow, 0, K, recv_weight != nullptr, r, wk);
   for (int k0 = 0;;) {
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
@@ -125,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     }
     k0 += KC;
     if (k0 >= K) break;
-    load_rows<KC>(srow, wrow, k0, K, want_w, r, wk);
+    load_rows<KC>(srow, wrow, k0, K, recv_weight != nullptr, r, wk);
   }
 }
 
@@ -153,13 +197,18 @@ hipError_t launch_dispatch_fp8(const uint16_t* x, int32_t T, int32_t H, int32_t 
   if (n_items == 0) return hipSuccess;
   const dim3 grid((n_items + kThreads - 1) / kThreads), block(kThreads);
   const bool nt = static_cast<size_t>(T) * H * 2 >= kStreamingTokenBytes;
-#define EP_DISPATCH_FP8(KV)                                                                                 \
-  if (nt)                                                                                                   \
-    hipLaunchKernelGGL((dispatch_fp8_kernel<KV, true>), grid, block, 0, stream, x, n_items, vpt, H, K, slot, w, \
-                       recv, recv_scale, recv_weight);                                                      \
-  else                                                                                                      \
-    hipLaunchKernelGGL((dispatch_fp8_kernel<KV, false>), grid, block, 0, stream, x, n_items, vpt, H, K, slot, w, \
-                       recv, recv_scale, recv_weight)
+  // wavefronts inside one token (vpt a multiple of 64: H a multiple of 1024)
+  // and 16-byte pieces of the scale rows (G a multiple of 4, aligned base)
+  const bool ws = vpt % kWave == 0 && (H / kGroup) % 4 == 0 && (reinterpret_cast<uintptr_t>(recv_scale) & 15) == 0;
+#define EP_DISPATCH_FP8_V(KV, NTV, WSV)                                                                           \
+  hipLaunchKernelGGL((dispatch_fp8_kernel<KV, NTV, WSV>), grid, block, 0, stream, x, n_items, vpt, H, K, slot, w, \
+                     recv, recv_scale, recv_weight)
+#define EP_DISPATCH_FP8(KV)                                              \
+  if (nt) {                                                              \
+    if (ws) EP_DISPATCH_FP8_V(KV, true, true); else EP_DISPATCH_FP8_V(KV, true, false);   \
+  } else {                                                               \
+    if (ws) EP_DISPATCH_FP8_V(KV, false, true); else EP_DISPATCH_FP8_V(KV, false, false); \
+  }
   switch (K) {
     case 1: { EP_DISPATCH_FP8(1); } break;
     case 2: { EP_DISPATCH_FP8(2); } break;
@@ -169,6 +218,7 @@ hipError_t launch_dispatch_fp8(const uint16_t* x, int32_t T, int32_t H, int32_t 
     default: { EP_DISPATCH_FP8(0); } break;
   }
 #undef EP_DISPATCH_FP8
+#undef EP_DISPATCH_FP8_V
   return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@ def test_summarizer_scales_counters_and_guards_by_source_hash(tmp_path, monkeypa
     monkeypatch.setattr(bench, "PROFILES", str(prof))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(prof / "traffic.txt"))
     names = {"layout": "void ep::(anonymous namespace)::layout_fused<16, true, int>(int const*)",
-             "dispatch": "void ep::(anonymous namespace)::dispatch_fp8_kernel<8, true>(unsigned short const*)",
+             "dispatch": "void ep::(anonymous namespace)::dispatch_fp8_kernel<8, true, true>(unsigned short const*)",
              "combine": "void ep::(anonymous namespace)::combine_kernel<8, false, true>(unsigned short const*)"}
     copy = "__amd_rocclr_copyBuffer"
     _write_csv(str(out / "prof_trace" / "t_kernel_stats.csv"),

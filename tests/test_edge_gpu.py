@@ -194,3 +194,43 @@ def test_debug_check_rejects_ids_outside_minus_one_to_e(gpu, monkeypatch):
     monkeypatch.setattr(api, "DEBUG_CHECK", False)
     counts, offsets, slot, src = gpu_layout(ep, idx, E)  # 16 is masked
     assert np.array_equal(host(slot), oracle.dispatch_layout(idx, E)[2])
+
+
+@pytest.mark.parametrize("T,H,scale_offset,K", [(300, 7168, 0, 8), (300, 7168, 1, 8), (300, 2048, 3, 8),
+                                                 (300, 1536, 0, 8), (300, 512, 0, 8), (300, 2048, 0, 10),
+                                                 (300, 1024, 1, 10), (1200, 7168, 0, 8), (1200, 7168, 1, 8),
+                                                 (1200, 7168, 0, 10), (6000, 1536, 0, 8)])
+def test_scale_store_paths(gpu, T, H, scale_offset, K):
+    """FP8 scales are written 32 bytes per row by each wavefront when H is a
+    multiple of 1024 and recv_scale is 16-byte aligned, else one lane per
+    group: both against the oracle, the second forced by a recv_scale that
+    starts scale_offset floats past an aligned address.  From 16 MB of tokens
+    (T=1200 at 7168, T=6000 at 1536) the stores are non-temporal.  K=10 takes
+    the kernel that walks a token's entries 8 at a time; the received
+    weights ride along in every case."""
+    ep = gpu
+    rng = np.random.default_rng(T + H + scale_offset + K)
+    E = 64
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    idx[rng.random((T, K)) < 0.05] = -1
+    w = rng.random((T, K), dtype=np.float32)
+    x = rand_x(T, H, seed=H)
+    print("case scale stores T=%d H=%d offset=%d K=%d" % (T, H, scale_offset, K), flush=True)
+    counts, offsets, slot, src = gpu_layout(ep, idx, E)
+    R, G = T * K, H // 128
+    recv = torch.full((R, H), SENT_U8, dtype=torch.uint8, device="cuda")
+    store = torch.full((R * G + 4,), -3.0, dtype=torch.float32, device="cuda")
+    scale = store[scale_offset:scale_offset + R * G].view(R, G)
+    assert (scale.data_ptr() % 16 == 0) == (scale_offset == 0)
+    rw = torch.full((R,), -5.0, dtype=torch.float32, device="cuda")
+    ep.ep_dispatch(to_dev(x.view(np.int16)), slot, to_dev(w), ep.EP_RECV_FP8_E4M3_G128, recv, scale, rw)
+    oc, oo, oslot, osrc = oracle.dispatch_layout(idx, E)
+    orecv, oscale, orw = oracle.dispatch_fp8(x, oslot, topk_weights=w)
+    nv = int(oo[-1])
+    assert np.array_equal(host(recv)[:nv], orecv[:nv])
+    assert np.array_equal(host(scale)[:nv].view(np.uint32), oscale[:nv].view(np.uint32))
+    assert np.array_equal(host(rw)[:nv].view(np.uint32), orw[:nv].view(np.uint32))
+    assert np.all(host(rw)[nv:] == -5.0)
+    # nothing written outside the scale rows of valid entries
+    rest = host(store)
+    assert np.all(rest[:scale_offset] == -3.0) and np.all(rest[scale_offset + nv * G:] == -3.0)
