@@ -1,11 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE dispatch/combine hot path on one MI355X.
 
-A step is one pass of the whole path over one batch: ep_dispatch_layout ->
-ep_dispatch (FP8 E4M3, one scale per 128 channels) -> ep_combine (BF16),
-on the prefill workload of the pages' normal-kernel setting (4096 tokens,
-hidden 7168, 256 experts in 8 groups, top-4 groups, top-8 experts).  Inputs
-are seeded synthetic tensors already resident in HBM when timing starts.
+A step is one pass of the whole path over one batch: ep_layout_dispatch
+(the layout and the FP8 E4M3 dispatch, one scale per 128 channels, in one
+launch) -> ep_combine (BF16), on the prefill workload of the pages'
+normal-kernel setting (4096 tokens, hidden 7168, 256 experts in 8 groups,
+top-4 groups, top-8 experts).  The same step as three calls
+(ep_dispatch_layout -> ep_dispatch -> ep_combine) is timed beside it.
+Inputs are seeded synthetic tensors already resident in HBM when timing
+starts.
 
     python bench.py [--steps K] [--warmup W]        # one JSON line
     python bench.py --workload hbm|skew|decode      # a JSON line for another configuration
@@ -41,9 +44,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = sorted("combine_ep_dispatch_amd/csrc/" + f for f in os.listdir(os.path.join(ROOT, "combine_ep_dispatch_amd", "csrc"))
                         if f.endswith((".hip", ".h")))
 TRAFFIC_FILE = os.path.join(PROFILES, "prefill_4096x7168_top8_counter_traffic.txt")
-# the prefill step's kernels as they appear in the profile
-STEP_KERNELS = {"layout": "layout_fused<16, true, int>", "dispatch": "dispatch_fp8_kernel<8, true, true>",
+# the prefill step's kernels as they appear in the profile, and the separate
+# layout and dispatch kernels of the three-call form, timed beside them
+STEP_KERNELS = {"layout_dispatch": "layout_dispatch_chunked<16, true, int, true, true, true>",
                 "combine": "combine_kernel<8, false, true>"}
+REF_KERNELS = {"layout": "layout_fused<16, true, int>", "dispatch": "dispatch_fp8_kernel<8, true, true>"}
+PROFILED_KERNELS = dict(STEP_KERNELS, **REF_KERNELS)
 
 
 def backward_bytes(T, H, K):
@@ -129,6 +135,7 @@ class Setup:
         self.ep.ep_combine(self.y, self.slot, self.w, self.out, num_rows=self.rows)
 
     def step(self):
+        """The three-call form: layout, dispatch, combine."""
         self.layout()
         self.dispatch()
         self.combine()
@@ -143,12 +150,13 @@ class Setup:
         return self._plan
 
     def layout_dispatch(self):
-        # one call for layout + dispatch (one launch up to 3072 entries)
+        # one call for layout + dispatch (one launch up to 65536 entries)
         self.ep.ep_layout_dispatch(self.idx, self.x, None, self.wl.E, self.capacity, self.fmt, self.counts,
                                    None if self.capacity else self.offsets, self.slot, self.src, self.recv,
                                    self.scale, None, self.ws)
 
     def step_fused(self):
+        """Layout and dispatch in one call, then combine."""
         self.layout_dispatch()
         self.combine()
 
@@ -168,36 +176,42 @@ class Setup:
                                     num_rows=self.rows)
 
 
-def time_steps(torch, s, steps, warmup):
+def time_steps(torch, s, steps, warmup, fused=False):
     """K steps bracketed by synchronisation, timed with HIP events on the
-    stream the kernels are launched on; then, for each of the three calls,
-    K back-to-back launches of it (bare C calls on the same inputs) between
-    two events: its mean launch duration, the kernel plus one launch gap.
-    An event recorded between every two calls would add ~5 µs to each
-    interval on MI355X."""
+    stream the kernels are launched on; then, for each call, K back-to-back
+    launches of it (bare C calls on the same inputs) between two events:
+    its mean launch duration, the kernel plus one launch gap.  An event
+    recorded between every two calls would add ~5 µs to each interval on
+    MI355X.  fused: the step is ep_layout_dispatch + ep_combine, and the
+    separate layout and dispatch kernels are timed too; else the three
+    calls."""
     stream = torch.cuda.current_stream()
+    step = s.step_fused if fused else s.step
     for _ in range(warmup):
-        s.step()
+        step()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     a.record(stream)
     for _ in range(steps):
-        s.step()
+        step()
     b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     us_step = a.elapsed_time(b) * 1e3 / steps
     plan = s.bare()
     plan.layout()
-    per = {name: time_loop(torch, fn, steps, 1)
-           for name, fn in (("layout", plan.layout), ("dispatch", plan.dispatch), ("combine", plan.combine))}
+    calls = [("layout", plan.layout), ("dispatch", plan.dispatch), ("combine", plan.combine)]
+    if fused:
+        calls = [("layout_dispatch", plan.layout_dispatch)] + calls
+    per = {name: time_loop(torch, fn, steps, 1) for name, fn in calls}
     return us_step, per, wall
 
 
 def time_distribution(torch, s, reps, flush_bytes=0):
-    """Per-step and per-kernel durations over `reps` steps, each step timed
-    on its own with HIP events between the three calls (launch stream).
+    """Per-step and per-call durations over `reps` steps (ep_layout_dispatch
+    then ep_combine), each step timed on its own with HIP events between
+    the calls (launch stream).
     flush_bytes > 0: before every step a device read of that many bytes (a
     reduction, outside the timed region) evicts the 256 MB Infinity Cache,
     so the step starts from HBM.  A write fill would evict it too, but
@@ -207,26 +221,23 @@ def time_distribution(torch, s, reps, flush_bytes=0):
     stream = torch.cuda.current_stream()
     scratch = torch.ones(flush_bytes // 4, dtype=torch.int32, device="cuda") if flush_bytes else None
     for _ in range(3):
-        s.step()
+        s.step_fused()
     torch.cuda.synchronize()
     marks = []
     for _ in range(reps):
         if scratch is not None:
             scratch.max()
-        m = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        m = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         m[0].record(stream)
-        s.layout()
+        s.layout_dispatch()
         m[1].record(stream)
-        s.dispatch()
-        m[2].record(stream)
         s.combine()
-        m[3].record(stream)
+        m[2].record(stream)
         marks.append(m)
     torch.cuda.synchronize()
-    series = {"step": [m[0].elapsed_time(m[3]) * 1e3 for m in marks],
-              "layout": [m[0].elapsed_time(m[1]) * 1e3 for m in marks],
-              "dispatch": [m[1].elapsed_time(m[2]) * 1e3 for m in marks],
-              "combine": [m[2].elapsed_time(m[3]) * 1e3 for m in marks]}
+    series = {"step": [m[0].elapsed_time(m[2]) * 1e3 for m in marks],
+              "layout_dispatch": [m[0].elapsed_time(m[1]) * 1e3 for m in marks],
+              "combine": [m[1].elapsed_time(m[2]) * 1e3 for m in marks]}
     del scratch
 
     def pct(v, q):
@@ -275,9 +286,9 @@ def time_graph(torch, step, replays, steps_per_graph=1):
 
 
 def read_traffic():
-    """HBM bytes per launch of the step's kernels ({"layout", "dispatch",
-    "combine"}) from the committed rocprofv3 counter summary, or None when
-    any kernel source changed since the counters were taken."""
+    """HBM bytes per launch of the profiled prefill kernels (the keys of
+    PROFILED_KERNELS) from the committed rocprofv3 counter summary, or None
+    when any kernel source changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -288,7 +299,7 @@ def read_traffic():
     if vals.get("source_sha256") != source_hash(KERNEL_SOURCES):
         return None
     try:
-        return {step: float(vals["hbm_bytes_per_launch[%s]" % step]) for step in STEP_KERNELS}
+        return {step: float(vals["hbm_bytes_per_launch[%s]" % step]) for step in PROFILED_KERNELS}
     except (KeyError, ValueError):
         return None
 
@@ -335,7 +346,8 @@ def cpu_baseline(wl, budget_s):
 def profile_pass(ep, torch, workload="prefill"):
     """Short run for rocprofv3: a plain 1 GiB device copy (counter
     calibration: known bytes read and written), then 5 steps of the
-    workload (prefill by default)."""
+    workload (prefill by default): three calls, then layout and dispatch in
+    one call."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     b = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -346,9 +358,8 @@ def profile_pass(ep, torch, workload="prefill"):
     s = Setup(ep, torch, workload, 0)
     for _ in range(5):
         s.step()
-    if workload == "decode":
-        for _ in range(5):
-            s.step_fused()
+    for _ in range(5):
+        s.step_fused()
     if workload == "prefill":
         s.backward_buffers(torch)
         for _ in range(3):
@@ -430,6 +441,7 @@ def summarize_profile(dirname):
     f_write = copy_kib / avg[("__amd_rocclr_copyBuffer", "WRITE_SIZE")]
     T, H, E, K = 4096, 7168, 256, 8
     alg = dict(zip(("layout", "dispatch_fp8_kernel", "combine_kernel"), alg_bytes(T, H, E, K, True)))
+    alg["layout_dispatch_chunked"] = alg["layout"] + alg["dispatch_fp8_kernel"]
     lines = ["HBM traffic per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (two separate --pmc runs),",
              "prefill workload (4096 x 7168, 256 experts, top-8, FP8 dispatch, BF16 combine).", "",
              "commands:", PROFILE_COMMANDS,
@@ -438,7 +450,8 @@ def summarize_profile(dirname):
                                       avg[("__amd_rocclr_copyBuffer", "WRITE_SIZE")]),
              "fetch_scale: %.4f" % f_fetch, "write_scale: %.4f" % f_write, ""]
     d_bwd, _ = backward_bytes(T, H, K)
-    known = (("layout", alg_bytes(T, H, E, K, True)[0]),
+    known = (("layout_fused", alg["layout"]),
+             ("layout_dispatch_chunked", alg["layout_dispatch_chunked"]),
              ("dispatch_fp8_kernel", alg["dispatch_fp8_kernel"]),
              ("combine_kernel<8, false,", alg["combine_kernel"]),
              ("combine_kernel<8, true,", d_bwd),  # ep_dispatch_backward
@@ -450,15 +463,16 @@ def summarize_profile(dirname):
             if fk is None or wk is None:
                 continue
             fb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
-            lines.append("%-32s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
+            lines.append("%-58s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
                          % (kern, fb, wb, fb + wb, a, (fb + wb) / a))
     totals = {}
     for kern in {k for (k, c) in avg}:
         fk, wk = avg.get((kern, "FETCH_SIZE")), avg.get((kern, "WRITE_SIZE"))
         if fk is not None and wk is not None:
             totals[kern] = fk * 1024 * f_fetch + wk * 1024 * f_write
-    lines += ["", "the prefill step's kernels (combine is the roofline's dominant kernel):"]
-    lines += ["hbm_bytes_per_launch[%s]: %.0f" % (step, totals[kern]) for step, kern in STEP_KERNELS.items()]
+    lines += ["", "the prefill step's kernels (combine is the roofline's dominant kernel), then the separate",
+              "layout and dispatch kernels of the three-call form:"]
+    lines += ["hbm_bytes_per_launch[%s]: %.0f" % (step, totals[kern]) for step, kern in PROFILED_KERNELS.items()]
     lines += ["source_sha256: %s" % source_hash(KERNEL_SOURCES),
               "(sha256 prefix of every file under combine_ep_dispatch_amd/csrc; bench.py reports counter bytes "
               "only while it matches)"]
@@ -498,14 +512,14 @@ def summarize_bench_run(dirname, rows, short):
              "Under the tracer every launch costs several microseconds more, which inflates the back-to-back",
              "figure of a kernel as short as the layout (and the decode-size timings of that run); the",
              "prefill dispatch and combine are long enough not to notice.", "", "commands:", PROFILE_COMMANDS,
-             "%-34s %6s %14s %14s %8s" % ("kernel", "calls", "rocprof_avg_us", "bench_us", "ratio")]
-    for step, kern in STEP_KERNELS.items():
+             "%-58s %6s %14s %14s %8s" % ("kernel", "calls", "rocprof_avg_us", "bench_us", "ratio")]
+    for step, kern in PROFILED_KERNELS.items():
         r = stats.get(kern)
         if r is None:
             continue
         prof_us = float(r["AverageNs"]) / 1e3
         bench_us = rec["kernel_us"][step]
-        lines.append("%-34s %6s %14.2f %14.2f %8.3f" % (kern, r["Calls"], prof_us, bench_us, bench_us / prof_us))
+        lines.append("%-58s %6s %14.2f %14.2f %8.3f" % (kern, r["Calls"], prof_us, bench_us, bench_us / prof_us))
     lines += ["", "bench line of that run: value %s %s, us_per_step %s, roofline %s"
               % (rec["value"], rec["unit"], rec["us_per_step"], json.dumps(rec["roofline"]))]
     with open(os.path.join(PROFILES, BENCH_RUN_FILE), "w") as f:
@@ -521,7 +535,7 @@ def other_workload(ep, torch, args):
     graph_us = time_graph(torch, s.step, 20 if s.wl.T > 8192 else 200)
     total = lay_b + dis_b + com_b
     wl = s.wl
-    rec = {"metric": "step µs and algorithmic GB/s", "workload": args.workload,
+    rec = {"metric": "step µs and algorithmic GB/s (three calls)", "workload": args.workload,
            "config": {"tokens": wl.T, "hidden": wl.H, "experts": wl.E, "top_k": wl.K,
                       "dispatch": "fp8" if wl.fp8 else "bf16"},
            "us_per_step": round(us_step, 2), "us_per_step_graph": round(graph_us, 2),
@@ -530,9 +544,13 @@ def other_workload(ep, torch, args):
            "kernel_GBs": {"dispatch": round(dis_b / per_kernel["dispatch"] / 1e3, 1),
                           "combine": round(com_b / per_kernel["combine"] / 1e3, 1)},
            "kernel_alg_bytes": {"layout": lay_b, "dispatch": dis_b, "combine": com_b}}
-    if wl.T * wl.K <= 3072:
-        # small batches: the one-launch layout + dispatch through StepPlan
-        plan = ep.StepPlan(s.idx, s.w, s.x, wl.E, fp8=wl.fp8, y=s.y)
+    # layout and dispatch in one call (one launch up to 65536 entries), then combine
+    fused_us = time_loop(torch, s.step_fused, args.steps, args.warmup)
+    rec["us_per_step_fused"] = round(fused_us, 2)
+    rec["GBs_fused"] = round(total / fused_us / 1e3, 1)
+    if wl.T * wl.K <= 65536:
+        plan = s.bare()
+        rec["kernel_us"]["layout_dispatch"] = round(time_loop(torch, plan.layout_dispatch, args.steps, 1), 2)
         rec["us_per_step_fused_step_plan"] = round(time_loop(torch, plan.step, args.steps, args.warmup), 2)
     print(json.dumps(rec), flush=True)
     return 0
@@ -579,10 +597,11 @@ def main():
 
     s = Setup(ep, torch, "prefill", 0)
     lay_b, dis_b, com_b = s.bytes
-    us_step, per_kernel, wall = time_steps(torch, s, args.steps, args.warmup)
+    us_step, per_kernel, wall = time_steps(torch, s, args.steps, args.warmup, fused=True)
+    us_three = time_loop(torch, s.step, args.steps, args.warmup)
     total_b = lay_b + dis_b + com_b
     gbs = total_b / (us_step * 1e-6) / 1e9
-    graph_us = time_graph(torch, s.step, 50)
+    graph_us = time_graph(torch, s.step_fused, 50)
     dist = {"warm": time_distribution(torch, s, 50), "flushed": time_distribution(torch, s, 50, 512 << 20)}
     s.backward_buffers(torch)
     db_b, cb_b = backward_bytes(s.wl.T, s.wl.H, s.wl.K)
@@ -630,13 +649,17 @@ def main():
                                "top-8, FP8 E4M3 dispatch (1 scale / 128 ch) + BF16 combine, seed 0",
                    "tokens": s.wl.T, "hidden": s.wl.H, "experts": s.wl.E, "top_k": s.wl.K},
         "us_per_step": round(us_step, 2),
+        "step": "ep_layout_dispatch (layout + FP8 dispatch, one launch) + ep_combine",
         "us_per_step_graph": round(graph_us, 2),
+        "us_per_step_three_calls": round(us_three, 2),
         "kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "kernel_us_method": "mean of K back-to-back launches of each kernel, HIP events on the launch stream "
-                            "(kernel plus one launch gap)",
-        "kernel_alg_bytes": {"layout": lay_b, "dispatch": dis_b, "combine": com_b},
-        "step_distribution_us": dict(dist, note="50 steps each timed alone (events between the calls); flushed: "
-                                                "a 512 MB device read before every step evicts the Infinity Cache"),
+                            "(kernel plus one launch gap); layout and dispatch are the three-call form's kernels",
+        "kernel_alg_bytes": {"layout_dispatch": lay_b + dis_b, "combine": com_b, "layout": lay_b,
+                             "dispatch": dis_b},
+        "step_distribution_us": dict(dist, note="50 steps each timed alone (events between the two calls); "
+                                                "flushed: a 512 MB device read before every step evicts the "
+                                                "Infinity Cache"),
         "flushed_GBs_at_median": round(total_b / dist["flushed"]["step"]["median"] / 1e3, 1),
         "decode_us_per_step": decode[0]["fused"]["stream_step_plan"],
         "decode_step": "128 tokens x 7168, 256 experts, top-8, FP8: ep_layout_dispatch + ep_combine through "
@@ -654,7 +677,7 @@ def main():
         rec["roofline"]["traffic_GBs"] = round(traffic["combine"] / (comb_us * 1e-6) / 1e9, 1)
         rec["counter_bytes_per_launch"] = {k: int(v) for k, v in traffic.items()}
         rec["counter_GBs"] = {k: round(traffic[k] / (per_kernel[k] * 1e-6) / 1e9, 1) for k in traffic}
-        rec["counter_GBs_step"] = round(sum(traffic.values()) / (us_step * 1e-6) / 1e9, 1)
+        rec["counter_GBs_step"] = round(sum(traffic[k] for k in STEP_KERNELS) / (us_step * 1e-6) / 1e9, 1)
     rec["context_pages"] = {
         "note": "DeepEP on H800, multi-GPU all-to-all over interconnects; context, not a target",
         "normal_kernels_nvlink_GBs": "153-158", "normal_kernels_rdma_GBs": "43-47",

@@ -177,7 +177,7 @@ def ep_dispatch(x, slot, topk_weights, format, recv_x, recv_scale=None, recv_wei
 def ep_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format, tokens_per_expert,
                        expert_offset, slot, src_token, recv_x, recv_scale=None, recv_weight=None, workspace=None,
                        stream=None):
-    """Layout and dispatch in one call (one launch up to 3072 entries).
+    """Layout and dispatch in one call (one launch up to 65536 entries).
     capacity 0: packed layout (expert_offset [E+1], src_token [T*K], T*K
     receive rows); capacity > 0: padded layout (expert_offset None,
     src_token [E*capacity], E*capacity receive rows)."""

@@ -20,7 +20,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libep.so")
-SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "fused.hip", "combine.hip", "combine_backward.hip"]
+SOURCES = ["ep_api.hip", "layout.hip", "layout_dispatch.hip", "dispatch.hip", "fused.hip", "combine.hip",
+           "combine_backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

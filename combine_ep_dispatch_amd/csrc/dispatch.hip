@@ -31,12 +31,6 @@ namespace ep {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr size_t kStreamingTokenBytes = size_t(16) << 20;  // from here on, non-temporal token loads
-
-template <bool NT>
-__device__ __forceinline__ u32x4 load_token(const u32x4* p) {
-  return NT ? __builtin_nontemporal_load(p) : *p;
-}
 
 // Receive rows (and weights) of entries k0 .. k0+KC-1 of one token, loaded
 // together before any store so their latencies overlap.  The row loads
@@ -54,34 +48,6 @@ __device__ __forceinline__ void load_rows(const int32_t* __restrict__ srow, cons
   if (load_w) {
 #pragma unroll
     for (int j = 0; j < KC; ++j) wk[j] = k0 + j < K ? wrow[k0 + j] : 0.0f;
-  }
-}
-
-// The 8 group scales one wavefront covers, written 32 bytes per row: lanes
-// 0, 8, .., 56 hold them (after quantize16_e4m3), and lane j < KC writes
-// all 8 to its row rj, the token's j-th (loaded by that lane itself: a
-// select among the lanes' copies would be turned into an indexed array
-// in LDS).  For a wave that lies inside one token, with 16-byte-aligned
-// 32-byte pieces (checked at launch).
-template <int KC, bool NT>
-__device__ __forceinline__ void store_wave_scales(int32_t rj, float s, uint32_t v, uint32_t G,
-                                                  float* __restrict__ recv_scale) {
-  const int lane = threadIdx.x & (kWave - 1);
-  u32x4 lo, hi;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo[i] = __builtin_amdgcn_readlane(__float_as_uint(s), 8 * i);
-    hi[i] = __builtin_amdgcn_readlane(__float_as_uint(s), 8 * (i + 4));
-  }
-  if (lane < KC && rj >= 0) {
-    u32x4* dst = reinterpret_cast<u32x4*>(recv_scale + static_cast<size_t>(rj) * G + ((v - lane) >> 3));
-    if (NT) {
-      __builtin_nontemporal_store(lo, dst);
-      __builtin_nontemporal_store(hi, dst + 1);
-    } else {
-      dst[0] = lo;
-      dst[1] = hi;
-    }
   }
 }
 
@@ -134,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
       }
       if (want_w) recv_weight[r[j]] = wk[j];
     }
-    if (WS) store_wave_scales<KC, NT>(rj, s, v, G, recv_scale);
+    if (WS) store_wave_scales<NT>(rj, s, v, G, recv_scale);
     k0 += KC;
     if (k0 >= K) break;
     load_rows<KC>(srow, wrow, k0, K, recv_weight != nullptr, r, wk);

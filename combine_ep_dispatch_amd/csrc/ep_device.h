@@ -171,4 +171,43 @@ __device__ __forceinline__ u32x4 quantize16_e4m3(u32x4 a, u32x4 b, float& scale)
   return q;
 }
 
+// ---- dispatch stores ------------------------------------------------------
+
+// One 16-byte token load; NT: non-temporal (a token read once).
+template <bool NT>
+__device__ __forceinline__ u32x4 load_token(const u32x4* p) {
+  return NT ? __builtin_nontemporal_load(p) : *p;
+}
+
+// The 8 group scales one wavefront of FP8 work items covers (64 lanes of 16
+// channels: 8 whole 128-channel groups of one token, lanes 0, 8, .., 56
+// holding them after quantize16_e4m3), written 32 bytes per receive row:
+// each lane with a row (rj >= 0, one lane per row of the token, loaded by
+// that lane itself: a select among the lanes' copies would be turned into
+// an indexed array in LDS) stores all 8 to row rj.  v is this lane's work
+// item in the token, G = H/128; the 32-byte pieces must be 16-byte aligned
+// (G a multiple of 4, recv_scale 16-byte aligned).  Every lane of the
+// wavefront must call it.
+template <bool NT>
+__device__ __forceinline__ void store_wave_scales(int32_t rj, float s, uint32_t v, uint32_t G,
+                                                  float* __restrict__ recv_scale) {
+  const int lane = threadIdx.x & (kWave - 1);
+  u32x4 lo, hi;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = __builtin_amdgcn_readlane(__float_as_uint(s), 8 * i);
+    hi[i] = __builtin_amdgcn_readlane(__float_as_uint(s), 8 * (i + 4));
+  }
+  if (rj >= 0) {
+    u32x4* dst = reinterpret_cast<u32x4*>(recv_scale + static_cast<size_t>(rj) * G + ((v - lane) >> 3));
+    if (NT) {
+      __builtin_nontemporal_store(lo, dst);
+      __builtin_nontemporal_store(hi, dst + 1);
+    } else {
+      dst[0] = lo;
+      dst[1] = hi;
+    }
+  }
+}
+
 }  // namespace ep

@@ -37,16 +37,31 @@ hipError_t launch_combine_backward(const uint16_t* grad_out, const uint16_t* y, 
                                    const float* w, int32_t num_tokens, int32_t hidden, int32_t top_k,
                                    uint16_t* grad_y, float* grad_w, hipStream_t stream);
 
-// Layout and dispatch together (ep_layout_dispatch): one fused launch when
-// num_tokens * top_k <= kFusedMaxEntries, else launch_layout followed by the
-// dispatch kernel (then `workspace` must hold layout_workspace_bytes).
+// Layout and dispatch together (ep_layout_dispatch): the decode kernel when
+// num_tokens * top_k <= kFusedMaxEntries; up to kOneLaunchMaxEntries the
+// chunked kernel where its shape limits allow; else launch_layout followed by
+// the dispatch kernel (then `workspace` must hold layout_workspace_bytes).
 constexpr int kFusedMaxEntries = 3072;
+constexpr int kOneLaunchMaxEntries = 65536;  // the one-launch layout (no workspace)
 template <typename Idx>
 hipError_t launch_layout_dispatch(const Idx* topk_idx, const uint16_t* x, const float* topk_weights,
                                   int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
                                   int32_t capacity, bool fp8, int32_t* counts, int32_t* offsets, int32_t* slot,
                                   int32_t* src, void* recv, float* recv_scale, float* recv_weight,
                                   void* workspace, hipStream_t stream);
+
+// The chunked layout + dispatch kernel: returns false, launching nothing,
+// when the shape is outside its limits; else launches and sets *err.
+template <typename Idx>
+bool launch_layout_dispatch_chunked(const Idx* topk_idx, const uint16_t* x, const float* topk_weights,
+                                    int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
+                                    int32_t capacity, bool fp8, int32_t* counts, int32_t* offsets, int32_t* slot,
+                                    int32_t* src, void* recv, float* recv_scale, float* recv_weight,
+                                    hipStream_t stream, hipError_t* err);
+
+// Dispatch reads the tokens with non-temporal loads from this many bytes of
+// tokens on (they are read once); smaller batches are usually still cached.
+constexpr size_t kStreamingTokenBytes = size_t(16) << 20;
 
 hipError_t launch_cast_fp8(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 

@@ -38,8 +38,9 @@
 // (256 experts, top-8, hidden 7168) one launch takes 6.3 us against 4.0 +
 // 4.8 us for the two kernels at 1024 entries, 8.3 against 11.5 us at 2048
 // and 10.1 against 12.4 us at 3072, and breaks even at 4096; the path is
-// used up to 3072 entries, and larger batches run the layout kernels and
-// the dispatch kernel.
+// used up to 3072 entries.  Larger batches run the chunked kernel
+// (layout_dispatch.hip), or, past its limits, the layout kernels and the
+// dispatch kernel.
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -336,7 +337,11 @@ hipError_t launch_layout_dispatch(const Idx* topk_idx, const uint16_t* x, const 
                                   void* workspace, hipStream_t stream) {
   const int64_t n = static_cast<int64_t>(num_tokens) * top_k;
   if (n > kFusedMaxEntries) {
-    hipError_t e = launch_layout(topk_idx, static_cast<int32_t>(n), top_k, num_experts, capacity, counts, offsets,
+    hipError_t e = hipSuccess;
+    if (launch_layout_dispatch_chunked(topk_idx, x, topk_weights, num_tokens, hidden, top_k, num_experts, capacity,
+                                       fp8, counts, offsets, slot, src, recv, recv_scale, recv_weight, stream, &e))
+      return e;
+    e = launch_layout(topk_idx, static_cast<int32_t>(n), top_k, num_experts, capacity, counts, offsets,
                                  slot, src, workspace, stream);
     if (e != hipSuccess) return e;
     return fp8 ? launch_dispatch_fp8(x, num_tokens, hidden, top_k, slot, topk_weights, static_cast<uint8_t*>(recv),

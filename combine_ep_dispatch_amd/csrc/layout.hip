@@ -33,8 +33,8 @@
 //    histograms of earlier chunks per key (16 loads in flight per thread),
 //    scans the totals over keys and writes the rows.
 
-#include "ep_device.h"
 #include "ep_internal.h"
+#include "layout_device.h"
 
 namespace ep {
 namespace {
@@ -42,113 +42,8 @@ namespace {
 constexpr int kSingleMaxWaves = 8;  // the single-workgroup path launches at most 8 waves
 constexpr int kSingleMaxThreads = kSingleMaxWaves * 64;
 constexpr int kSingleMaxEntries = 1024;  // one workgroup, no workspace
-constexpr int kOneLaunchMaxEntries = 65536;  // one launch, no workspace
 constexpr int kMultiThreads = 256;
 constexpr int kMultiWaves = kMultiThreads / kWave;
-constexpr int kHistCopies = 4;  // one-launch layout: private histograms per lane & 3
-
-// The keys of this wavefront's entries p_begin + 64*i + lane (E past
-// p_end), loaded apart from the ranking so that a caller can issue the
-// loads early.
-template <int ITERS, typename Idx>
-__device__ __forceinline__ void load_wave_keys(const Idx* __restrict__ idx, int p_begin, int p_end, int E,
-                                               int (&e)[ITERS]) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int i = 0; i < ITERS; ++i) {
-    const int p = p_begin + i * kWave + lane;
-    e[i] = p < p_end ? expert_key(idx[p], E) : E;
-  }
-}
-
-// Rank ITERS consecutive 64-entry steps of this wavefront: entries
-// [p_begin, p_end) with keys e (from load_wave_keys).  lmask (E+1 lane
-// masks, all zero on entry and on exit) and cnt (E+1 running counts) are
-// this wave's LDS rows.  On return key[i] is the entry's key (E for masked,
-// -1 past p_end) and rank[i] its position among the wave's entries with
-// that key.
-//
-// Per step every in-range lane ORs its lane bit into lmask[key]; reading
-// lmask[key] back gives the set of lanes holding the same key (OR is
-// order-free, so the result is deterministic).  The rank is the number of
-// those lanes below this one plus the running count; the lowest such lane
-// advances the count and clears the mask.  LDS operations of one wavefront
-// execute in program order, which is all the step relies on.
-template <int ITERS>
-__device__ __forceinline__ void rank_wave_keys(const int (&e)[ITERS], int p_begin, int p_end, uint64_t* lmask,
-                                               int* cnt, int (&key)[ITERS], int (&rank)[ITERS]) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int i = 0; i < ITERS; ++i) {
-    if (p_begin + i * kWave >= p_end) {  // wave-uniform: nothing left
-      key[i] = -1;
-      rank[i] = 0;
-      continue;
-    }
-    const int p = p_begin + i * kWave + lane;
-    const bool inr = p < p_end;
-    const int k = e[i];
-    if (inr) __hip_atomic_fetch_or(&lmask[k], 1ull << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-    __builtin_amdgcn_wave_barrier();
-    const uint64_t same = inr ? __hip_atomic_load(&lmask[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT) : 0ull;
-    const int below = static_cast<int>(lanes_below(same));
-    const int pre = inr ? cnt[k] : 0;
-    __builtin_amdgcn_wave_barrier();
-    if (inr && below == 0) {
-      cnt[k] = pre + static_cast<int>(__popcll(same));
-      __hip_atomic_store(&lmask[k], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-    }
-    __builtin_amdgcn_wave_barrier();
-    key[i] = inr ? k : -1;
-    rank[i] = pre + below;
-  }
-}
-
-// load_wave_keys then rank_wave_keys
-template <int ITERS, typename Idx>
-__device__ __forceinline__ void rank_wave_range(const Idx* __restrict__ idx, int p_begin, int p_end,
-                                                int E, uint64_t* lmask, int* cnt, int (&key)[ITERS],
-                                                int (&rank)[ITERS]) {
-  int e[ITERS];
-  load_wave_keys<ITERS>(idx, p_begin, p_end, E, e);
-  rank_wave_keys<ITERS>(e, p_begin, p_end, lmask, cnt, key, rank);
-}
-
-// Row of one entry whose rank among the entries of its key is `within`.
-// Packed layout (cap == 0): row off[k] + within; masked entries (k == E)
-// take the rows after the valid ones with src = -1.  Padded layout
-// (cap > 0): expert e owns rows e*cap .. e*cap+cap-1; entries ranked past
-// the capacity and masked entries get slot -1 and no row, and the unused
-// rows of an expert's block are not written.
-__device__ __forceinline__ void write_entry(int p, int k, int within, const int* off, int E, int K, int cap,
-                                            int32_t* __restrict__ slot, int32_t* __restrict__ src) {
-  const bool valid = k < E;
-  const int t = valid ? static_cast<int>(static_cast<uint32_t>(p) / static_cast<uint32_t>(K)) : -1;
-  if (cap == 0) {
-    const int pos = off[k] + within;
-    slot[p] = valid ? pos : -1;
-    src[pos] = t;
-  } else {
-    const bool keep = valid && within < cap;
-    slot[p] = keep ? k * cap + within : -1;
-    if (keep) src[k * cap + within] = t;
-  }
-}
-
-// Counts and offsets from the exclusive scan `off` of the per-key totals
-// (written by one workgroup); in the padded layout the count is clamped to
-// the capacity and there are no offsets.
-__device__ __forceinline__ void write_counts(const int* off, int E, int cap, int part, int32_t* __restrict__ counts,
-                                             int32_t* __restrict__ offsets) {
-  if (part != 0) return;
-  const int tid = threadIdx.x, bs = blockDim.x;
-  for (int j = tid; j < E; j += bs) {
-    const int total = off[j + 1] - off[j];
-    counts[j] = cap == 0 ? total : min(total, cap);
-  }
-  if (cap == 0)
-    for (int j = tid; j <= E; j += bs) offsets[j] = off[j];
-}
 
 template <int ITERS, typename Idx>
 __global__ __launch_bounds__(kSingleMaxThreads) void layout_single(
@@ -285,161 +180,17 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
   }
 }
 
-// One launch for the whole layout.  Block b owns the chunk of NW*64
-// consecutive entries starting at b*NW*64 (one 64-entry step per wave) and
-// ranks it as above; it also histograms all T*K entries with LDS atomic
-// adds (integer addition is order-free, so the counts are exact and
-// deterministic): entries before its chunk into `before`, the rest, its
-// chunk included, into `after`.  Then for every key: total = before +
-// after, offsets are the exclusive scan of the totals, and an entry's row
-// is offset + before + (own-chunk rank).  Every block reads all T*K ids
-// (from L2 after the first), which trades redundant on-chip work for the
-// second launch and the workspace.  Everything in the histogram step is
-// paid once per entry (32 per lane at 32768 entries), so it spends one LDS
-// atomic and its address per entry: which histogram takes a load's ids is
-// one block-uniform comparison per 16-byte load, and lanes spread over
-// kHistCopies private copies so that a hot expert's entries in one wave
-// collide on fewer addresses.  All blocks walk the ids in the same
-// order: one L2 miss per XCD then serves every block on it (a per-block
-// rotated start measured 1.7x slower with int64 ids).
-// V4: 16-byte id loads (ids aligned to 16 bytes): 4 int32 or 2 int64 ids each.
+// One launch for the whole layout: workgroup b owns the chunk of NW*64
+// consecutive entries from b*NW*64 (layout_chunk).
 template <int NW, bool V4, typename Idx>
 __global__ __launch_bounds__(NW * kWave) void layout_fused(
     const Idx* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src) {
   extern __shared__ uint64_t lds64[];
-  constexpr int kThreads = NW * kWave;
-  const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
-  const int nk = E + 1;
-  uint64_t* lmask = lds64;                             // [NW][nk]
-  int* cnt = reinterpret_cast<int*>(lmask + NW * nk);  // [NW][nk]
-  int* before = cnt + NW * nk;                         // [kHistCopies][nk], merged into copy 0
-  int* after = before + kHistCopies * nk;              // [kHistCopies][nk], copy 0 later totals and offsets
-  // clear the lane masks, running counts and histograms (callers sync)
-  auto clear_lds = [&]() {
-    for (int i = tid; i < NW * nk; i += kThreads) {
-      lmask[i] = 0;
-      cnt[i] = 0;
-    }
-    for (int i = tid; i < kHistCopies * nk; i += kThreads) {
-      before[i] = 0;
-      after[i] = 0;
-    }
-  };
-
-  const int c0 = blockIdx.x * kThreads;
-  const int c1 = min(R, c0 + kThreads);
-  // Histogram every entry: those before this block's chunk into `before`,
-  // the rest (the chunk itself included) into `after`, so the per-key total
-  // is before + after.  Lanes spread over kHistCopies private copies, so
-  // entries of one hot expert in one wave collide on fewer LDS addresses.
-  // this wave's 64 entries of the chunk, ranked after the histogram; their
-  // keys are loaded with the first batch of ids
-  const int p_begin = c0 + w * kWave, p_stop = min(c1, p_begin + kWave);
-  int own[1];
-  const int copy = (lane & (kHistCopies - 1)) * nk;
-  int* const hb = before + copy;
-  int* const ha = after + copy;
-  if constexpr (V4) {
-    // 16-byte loads of kPer ids each, 32 ids in flight per thread.  c0 is
-    // a multiple of the chunk size and so of kPer: each load lies wholly
-    // before or wholly at/after c0 (one block-uniform comparison per load),
-    // and the last R % kPer ids all lie at or after c0
-    constexpr int kPer = 16 / static_cast<int>(sizeof(Idx));
-    constexpr int kUnroll = 32 / kPer;
-    const int4* idx4 = reinterpret_cast<const int4*>(idx);
-    const int n4 = R / kPer, qb = c0 / kPer;
-    int4 e[kUnroll];
-    auto load_batch = [&](int q0) {
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int q = q0 + u * kThreads + tid;
-        e[u] = q < n4 ? idx4[q] : make_int4(0, 0, 0, 0);
-      }
-    };
-    // the first batch is loaded before the LDS is cleared, so the loads'
-    // latency overlaps the clearing and the waves' start (at 32768 int32 or
-    // int64 ids one batch is all of them); the empty asm keeps the compiler
-    // from sinking the loads below the clearing
-    load_batch(0);
-    load_wave_keys<1>(idx, p_begin, p_stop, E, own);
-    asm volatile("" ::: "memory");
-    clear_lds();
-    __syncthreads();
-    for (int q0 = 0;;) {
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int q = q0 + u * kThreads + tid;
-        if (q >= n4) continue;
-        int* const h = q < qb ? hb : ha;
-        int k4[kPer];
-        expert_keys16<Idx>(e[u], E, k4);
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) atomicAdd(&h[k4[j]], 1);
-      }
-      q0 += kThreads * kUnroll;
-      if (q0 >= n4) break;
-      load_batch(q0);
-    }
-    const int p = kPer * n4 + tid;  // the last R % kPer ids
-    if (p < R) atomicAdd(&ha[expert_key(idx[p], E)], 1);
-  } else {
-    load_wave_keys<1>(idx, p_begin, p_stop, E, own);
-    clear_lds();
-    __syncthreads();
-    constexpr int kUnroll = 16;
-    for (int q0 = 0; q0 < R; q0 += kThreads * kUnroll) {
-      int e[kUnroll];  // keys
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int p = q0 + u * kThreads + tid;
-        e[u] = p < R ? expert_key(idx[p], E) : E;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int p = q0 + u * kThreads + tid;
-        if (p < R) atomicAdd(&(p < c0 ? hb : ha)[e[u]], 1);
-      }
-    }
-  }
-
-  int key[1], rank[1];
-  rank_wave_keys<1>(own, p_begin, p_stop, lmask + w * nk, cnt + w * nk, key, rank);
-  __syncthreads();
-
-  for (int j = tid; j < nk; j += kThreads) {
-    int run = 0;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const int c = cnt[ww * nk + j];
-      cnt[ww * nk + j] = run;
-      run += c;
-    }
-    int b = 0, a = 0;
-#pragma unroll
-    for (int cp = 0; cp < kHistCopies; ++cp) {
-      b += before[cp * nk + j];
-      a += after[cp * nk + j];
-    }
-    before[j] = b;
-    after[j] = b + a;  // total: `after` counted this block's chunk too
-  }
-  __syncthreads();
-  block_exclusive_scan(after, nk);
-  write_counts(after, E, cap, blockIdx.x, counts, offsets);
-
-  const int k = key[0];
-  if (k >= 0) write_entry(p_begin + lane, k, before[k] + cnt[w * nk + k] + rank[0], after, E, K, cap, slot, src);
+  const int c0 = blockIdx.x * NW * kWave;
+  layout_chunk<NW, V4, Idx, false>(idx, R, K, E, cap, c0, min(R, c0 + NW * kWave), lds64, counts, offsets, slot,
+                                   src, [] {}, [](int) {});
 }
-
-size_t fused_lds_bytes(int nw, int E) {
-  const size_t nk = static_cast<size_t>(E) + 1;
-  return nw * nk * 12 + 2 * kHistCopies * nk * 4;
-}
-
-// LDS one workgroup may allocate on gfx950: the CU's whole 160 KB.  Up to
-// 512 experts the one-launch layout keeps 16 waves; at 1024, 8.
-constexpr size_t kLdsLimit = 160 * 1024;
 
 size_t single_lds_bytes(int nw, int E) {
   const size_t nk = static_cast<size_t>(E) + 1;
@@ -451,12 +202,6 @@ int single_waves(int E) {
   // to scan per key, two 64-entry steps each)
   int nw = kSingleMaxWaves;
   while (nw > 1 && single_lds_bytes(nw, E) > kLdsLimit) nw >>= 1;
-  return nw;
-}
-
-int fused_waves(int E) {
-  int nw = 16;
-  while (nw > 1 && fused_lds_bytes(nw, E) > kLdsLimit) nw >>= 1;
   return nw;
 }
 
@@ -501,10 +246,10 @@ hipError_t launch_layout(const Idx* topk_idx, int32_t rows, int32_t top_k, int32
     return hipGetLastError();
   }
   if (path == LayoutPath::kFused) {
-    const int nw = fused_waves(E);
+    const int nw = chunk_waves(E);
     const int chunk = nw * kWave;
     const dim3 grid((rows + chunk - 1) / chunk), block(chunk);
-    const size_t lds = fused_lds_bytes(nw, E);
+    const size_t lds = chunk_lds_bytes(nw, E);
     // 16-byte id loads: ids aligned to 16 bytes
     const bool v4 = (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0;
 #define EP_LAYOUT_FUSED_V(NW, V)                                                                                  \

@@ -108,7 +108,7 @@ class StepPlan:
         check("ep_dispatch", LIB.ep_dispatch(*self._dispatch_args))
 
     def layout_dispatch(self):
-        """layout() and dispatch() as one call (one launch up to 3072 entries)."""
+        """layout() and dispatch() as one call (one launch up to 65536 entries)."""
         check("ep_layout_dispatch", self._fn_layout_dispatch(*self._layout_dispatch_args))
 
     def combine(self):

@@ -188,7 +188,10 @@ ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, int32_t
  * Writes exactly what ep_dispatch_layout (capacity == 0) or
  * ep_dispatch_layout_padded (capacity > 0) followed by ep_dispatch would
  * write, bit for bit.  Up to 3072 entries (T*K) this is one kernel launch
- * (the decode sizes, where launch latency dominates); beyond, the same
+ * built for the decode sizes, where launch latency dominates; up to 65536
+ * entries another single launch, in which each workgroup lays out and
+ * dispatches its own tokens (when the shape allows: top_k <= 64, at most 8
+ * work items of each token per thread; else as beyond); beyond, the same
  * launches as the separate calls.
  *
  * topk_idx, tokens_per_expert, slot, src_token, workspace: as for

@@ -53,16 +53,16 @@ def test_summarizer_scales_counters_and_guards_by_source_hash(tmp_path, monkeypa
     out, prof = tmp_path / "out", tmp_path / "profiles"
     monkeypatch.setattr(bench, "PROFILES", str(prof))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(prof / "traffic.txt"))
-    names = {"layout": "void ep::(anonymous namespace)::layout_fused<16, true, int>(int const*)",
-             "dispatch": "void ep::(anonymous namespace)::dispatch_fp8_kernel<8, true, true>(unsigned short const*)",
-             "combine": "void ep::(anonymous namespace)::combine_kernel<8, false, true>(unsigned short const*)"}
+    names = {k: "void ep::(anonymous namespace)::%s(int const*)" % v for k, v in bench.PROFILED_KERNELS.items()}
     copy = "__amd_rocclr_copyBuffer"
     _write_csv(str(out / "prof_trace" / "t_kernel_stats.csv"),
                [{"Name": n, "Calls": 5, "AverageNs": 1000.0 * (i + 1), "MinNs": 900.0, "MaxNs": 1100.0}
                 for i, n in enumerate(names.values())])
     # calibration: the 1 GiB copy reads FETCH_SIZE 512 MiB (scale 2) and WRITE_SIZE 1 GiB (scale 1)
-    fetch = {copy: 524288.0, names["layout"]: 100.0, names["dispatch"]: 29000.0, names["combine"]: 230000.0}
-    write = {copy: 1048576.0, names["layout"]: 50.0, names["dispatch"]: 236000.0, names["combine"]: 57000.0}
+    fetch = {copy: 524288.0, names["layout"]: 100.0, names["dispatch"]: 29000.0, names["combine"]: 230000.0,
+             names["layout_dispatch"]: 29500.0}
+    write = {copy: 1048576.0, names["layout"]: 50.0, names["dispatch"]: 236000.0, names["combine"]: 57000.0,
+             names["layout_dispatch"]: 236500.0}
     for sub, counter, vals in (("prof_fetch", "FETCH_SIZE", fetch), ("prof_write", "WRITE_SIZE", write)):
         rows = []
         for n, v in vals.items():
@@ -72,8 +72,12 @@ def test_summarizer_scales_counters_and_guards_by_source_hash(tmp_path, monkeypa
     text = open(prof / "traffic.txt").read()
     assert "fetch_scale: 2.0000" in text and "write_scale: 1.0000" in text
     got = bench.read_traffic()
-    for step in ("layout", "dispatch", "combine"):
+    assert set(got) == {"layout_dispatch", "combine", "layout", "dispatch"}
+    for step in got:
         assert got[step] == fetch[names[step]] * 1024 * 2 + write[names[step]] * 1024
+    # the one-launch kernel is held against the layout's and the dispatch's bytes together
+    lay, dis, _ = bench.alg_bytes(4096, 7168, 256, 8, True)
+    assert ("algorithmic %12d B" % (lay + dis)) in text
     assert (prof / "prefill_4096x7168_top8_kernel_trace.txt").exists()
     # a source change invalidates the counter bytes
     stale = text.replace("source_sha256: ", "source_sha256: 0")
@@ -87,10 +91,10 @@ def test_bench_run_summary_pairs_profiler_and_bench_line(tmp_path, monkeypatch):
     os.makedirs(prof)
     monkeypatch.setattr(bench, "PROFILES", str(prof))
     stats = [{"Name": "void ep::(anonymous namespace)::%s(int)" % k, "Calls": 100, "AverageNs": ns, "MinNs": ns,
-              "MaxNs": ns} for k, ns in zip(bench.STEP_KERNELS.values(), (9000.0, 50000.0, 90000.0))]
+              "MaxNs": ns} for k, ns in zip(bench.PROFILED_KERNELS.values(), (54000.0, 90000.0, 9000.0, 50000.0))]
     _write_csv(str(out / "prof_bench" / "b_kernel_stats.csv"), stats)
     line = {"value": 1.0, "unit": "GB/s", "us_per_step": 150.0, "roofline": {"frac": 0.7},
-            "kernel_us": {"layout": 9.9, "dispatch": 50.5, "combine": 88.2}}
+            "kernel_us": {"layout_dispatch": 53.0, "combine": 88.2, "layout": 9.9, "dispatch": 50.5}}
     with open(out / "bench_under_rocprof.json", "w") as f:
         f.write("some profiler noise\n" + json.dumps(line) + "\n")
 

@@ -1,10 +1,10 @@
 """ep_layout_dispatch (layout and dispatch in one call) against the oracle.
 
 Bar: every output bit-exact, rows and entries the contract leaves alone
-still hold their sentinels.  Cases span the one-launch path (up to 3072
-entries) and both fallbacks beyond it, packed and padded layouts, FP8 and
-BF16, masked ids of every kind, generic top-k, ragged hidden sizes and the
-empty batch.
+still hold their sentinels.  Cases span the decode kernel (up to 3072
+entries) and the paths beyond it (the chunked kernel has its own file),
+packed and padded layouts, FP8 and BF16, masked ids of every kind, generic
+top-k, ragged hidden sizes and the empty batch.
 """
 
 import numpy as np
@@ -160,9 +160,9 @@ def test_empty_batch_writes_zero_counts(gpu):
 
 @pytest.mark.parametrize("T,K,cap", [(3073, 1, 0), (385, 8, 0), (512, 8, 0), (9000, 8, 0), (600, 8, 40)])
 def test_fallback_paths(gpu, T, K, cap):
-    """Past 3072 entries: the layout kernels then the dispatch kernel
-    (single-launch layout below 65536 entries, two-kernel layout with the
-    workspace beyond)."""
+    """Past 3072 entries: the chunked kernel up to 65536 entries, beyond
+    that the two-kernel layout (with the workspace) then the dispatch
+    kernel."""
     rng = np.random.default_rng(T + K)
     E, H = 256, 512
     idx = routing(rng, T, K, E, distinct=True, mask_frac=0.05)

@@ -65,7 +65,7 @@ def test_layout_paths(gpu, T, K, E, cap):
 @pytest.mark.parametrize("T,cap,fp8", [(128, 0, True), (128, 128, True), (128, 0, False), (384, 0, True),
                                        (600, 0, True), (64, 5, True)])
 def test_one_call_dispatch(gpu, T, cap, fp8):
-    """Fused kernel (up to 3072 entries) and the two-launch fallback."""
+    """Decode kernel (up to 3072 entries) and the chunked kernel beyond."""
     ep = gpu
     E, K, H = 256, 8, 7168
     rng = np.random.default_rng(T + cap)
