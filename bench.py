@@ -47,7 +47,7 @@ TRAFFIC_FILE = os.path.join(PROFILES, "prefill_4096x7168_top8_counter_traffic.tx
 # the prefill step's kernels as they appear in the profile, and the separate
 # layout and dispatch kernels of the three-call form, timed beside them
 STEP_KERNELS = {"layout_dispatch": "layout_dispatch_chunked<16, true, int, true, true, true>",
-                "combine": "combine_kernel<8, false, true>"}
+                "combine": "combine_burst_kernel<8, false>"}
 REF_KERNELS = {"layout": "layout_fused<16, true, int>", "dispatch": "dispatch_fp8_kernel<8, true, true>"}
 PROFILED_KERNELS = dict(STEP_KERNELS, **REF_KERNELS)
 
@@ -454,7 +454,9 @@ def summarize_profile(dirname):
              ("layout_dispatch_chunked", alg["layout_dispatch_chunked"]),
              ("dispatch_fp8_kernel", alg["dispatch_fp8_kernel"]),
              ("combine_kernel<8, false,", alg["combine_kernel"]),
+             ("combine_burst_kernel<8, false>", alg["combine_kernel"]),
              ("combine_kernel<8, true,", d_bwd),  # ep_dispatch_backward
+             ("combine_burst_kernel<8, true>", d_bwd),
              ("grad_rows_kernel", 2 * T * H + 8 * T * K + 2 * T * K * H),
              ("grad_weights_kernel", 2 * T * H + 2 * T * K * H + 8 * T * K))
     for prefix, a in known:

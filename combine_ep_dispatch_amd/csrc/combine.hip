@@ -21,6 +21,13 @@
 // 64 MB of gathered rows, e.g. decode: 14.7 MB) use plain accesses, which
 // hit rows still held in the caches (measured 3.1-3.3 against 3.8 us for
 // 128 tokens, top-8, hidden 7168).  No LDS, no MFMA.
+//
+// Large batches that fit one workgroup per CU (combine_burst_kernel): HBM
+// moves a stream of reads alone faster than one with writes mixed in, so
+// each 1024-lane workgroup owns ceil(T / CUs) consecutive tokens, keeps
+// its finished output vectors in registers (at most kBurstItems per lane)
+// and writes them all once its gathers are done.  The writes of all CUs
+// then come at the end, in one burst, instead of among the reads.
 
 // Gathered bytes from which the streaming accesses are used.
 constexpr size_t kStreamingBytes = size_t(64) << 20;
@@ -32,9 +39,12 @@ namespace ep {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBurstThreads = 1024;
+constexpr int kBurstItems = 14;  // output vectors held per lane (4 VGPRs each)
 
 // Adds the terms of k = k0 .. k0+KC-1 (those < K) to acc, in ascending k.
-template <int KC, bool NT>
+// UNIT: every weight 1 (wrow unused).
+template <int KC, bool UNIT, bool NT>
 __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y, const int32_t* __restrict__ srow,
                                                  const float* __restrict__ wrow, int k0, int K, int32_t H,
                                                  uint32_t v, float (&acc)[8]) {
@@ -44,7 +54,7 @@ __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y,
   for (int j = 0; j < KC; ++j) {
     const bool in = k0 + j < K;
     r[j] = in ? srow[k0 + j] : -1;
-    wk[j] = in ? (wrow != nullptr ? wrow[k0 + j] : 1.0f) : 0.0f;  // no weights: unit weights
+    wk[j] = UNIT ? 1.0f : (in ? wrow[k0 + j] : 0.0f);
   }
   u32x4 d[KC];
 #pragma unroll
@@ -86,9 +96,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
   if (KT > 0) {
-    accumulate_chunk<(KT > 0 ? KT : 1), NT>(y, srow, wrow, 0, K, H, v, acc);
+    accumulate_chunk<(KT > 0 ? KT : 1), UNIT, NT>(y, srow, wrow, 0, K, H, v, acc);
   } else {
-    for (int k0 = 0; k0 < K; k0 += 8) accumulate_chunk<8, NT>(y, srow, wrow, k0, K, H, v, acc);
+    for (int k0 = 0; k0 < K; k0 += 8) accumulate_chunk<8, UNIT, NT>(y, srow, wrow, k0, K, H, v, acc);
   }
   u32x4 o;
 #pragma unroll
@@ -100,6 +110,62 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
     *dst = o;
 }
 
+// Workgroup b: tokens b*tpb .. b*tpb+tpb-1, whose work items i*kBurstThreads
+// + tid, i < kBurstItems, this lane sums as combine_kernel does; the output
+// vectors are held until every item of the lane is summed, then written.
+template <int KT, bool UNIT>
+__global__ __launch_bounds__(kBurstThreads) void combine_burst_kernel(const uint16_t* __restrict__ y,
+                                                                      const int32_t* __restrict__ slot,
+                                                                      const float* __restrict__ w, int32_t T,
+                                                                      int32_t H, int32_t Krt, int32_t tpb,
+                                                                      uint16_t* __restrict__ out) {
+  const int K = KT > 0 ? KT : Krt;
+  const int tok0 = blockIdx.x * tpb;
+  const uint32_t vpt = static_cast<uint32_t>(H) / 8;
+  const uint32_t nitems = static_cast<uint32_t>(min(T - tok0, tpb)) * vpt;
+  u32x4 o[kBurstItems];
+#pragma unroll
+  for (int i = 0; i < kBurstItems; ++i) {
+    const uint32_t item = static_cast<uint32_t>(i * kBurstThreads) + threadIdx.x;
+    if (item < nitems) {
+      const uint32_t tl = item / vpt, v = item - tl * vpt;
+      const int32_t* srow = slot + static_cast<size_t>(tok0 + tl) * K;
+      const float* wrow = UNIT ? nullptr : w + static_cast<size_t>(tok0 + tl) * K;
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+      if (KT > 0) {
+        accumulate_chunk<(KT > 0 ? KT : 1), UNIT, true>(y, srow, wrow, 0, K, H, v, acc);
+      } else {
+        for (int k0 = 0; k0 < K; k0 += 8) accumulate_chunk<8, UNIT, true>(y, srow, wrow, k0, K, H, v, acc);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[i][q] = f32_to_bf16_rne(acc[2 * q]) | (f32_to_bf16_rne(acc[2 * q + 1]) << 16);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kBurstItems; ++i) {
+    const uint32_t item = static_cast<uint32_t>(i * kBurstThreads) + threadIdx.x;
+    if (item < nitems) {
+      const uint32_t tl = item / vpt, v = item - tl * vpt;
+      __builtin_nontemporal_store(o[i], reinterpret_cast<u32x4*>(out + static_cast<size_t>(tok0 + tl) * H) + v);
+    }
+  }
+}
+
+// CUs of the current device (read once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w, int32_t T, int32_t H,
@@ -109,6 +175,27 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w
   if (n_items == 0) return hipSuccess;
   const dim3 grid((n_items + kThreads - 1) / kThreads), block(kThreads);
   const bool nt = static_cast<size_t>(T) * K * H * 2 >= kStreamingBytes;
+  // burst: large batches whose tokens fit one workgroup per CU
+  const int cus = nt ? device_cus() : 0;
+  const int tpb = cus > 0 ? (T + cus - 1) / cus : 0;
+  if (tpb > 0 && static_cast<int64_t>(tpb) * vpt <= static_cast<int64_t>(kBurstItems) * kBurstThreads) {
+    const dim3 bgrid((T + tpb - 1) / tpb), bblock(kBurstThreads);
+#define EP_COMBINE_BURST(KV)                                                                                 \
+  if (w == nullptr)                                                                                          \
+    hipLaunchKernelGGL((combine_burst_kernel<KV, true>), bgrid, bblock, 0, stream, y, slot, w, T, H, K, tpb, out); \
+  else                                                                                                       \
+    hipLaunchKernelGGL((combine_burst_kernel<KV, false>), bgrid, bblock, 0, stream, y, slot, w, T, H, K, tpb, out)
+    switch (K) {
+      case 1: { EP_COMBINE_BURST(1); } break;
+      case 2: { EP_COMBINE_BURST(2); } break;
+      case 4: { EP_COMBINE_BURST(4); } break;
+      case 6: { EP_COMBINE_BURST(6); } break;
+      case 8: { EP_COMBINE_BURST(8); } break;
+      default: { EP_COMBINE_BURST(0); } break;
+    }
+#undef EP_COMBINE_BURST
+    return hipGetLastError();
+  }
 #define EP_COMBINE_NT(KV, U, NTV) \
   hipLaunchKernelGGL((combine_kernel<KV, U, NTV>), grid, block, 0, stream, y, slot, w, n_items, vpt, H, K, out)
 #define EP_COMBINE(KV)                                                     \

@@ -108,5 +108,5 @@ def test_bench_run_summary_pairs_profiler_and_bench_line(tmp_path, monkeypatch):
     assert bench.summarize_bench_run(str(out), rows, lambda n: n.replace("void ep::(anonymous namespace)::", "")
                                      .split("(")[0])
     text = open(prof / bench.BENCH_RUN_FILE).read()
-    assert "combine_kernel<8, false, true>" in text and " 0.980" in text  # 88.2 / 90.0
+    assert bench.STEP_KERNELS["combine"] in text and " 0.980" in text  # 88.2 / 90.0
     assert " 1.100" in text  # layout 9.9 / 9.0

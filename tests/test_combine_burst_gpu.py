@@ -1,0 +1,73 @@
+"""Combine of large batches (from 64 MB of gathered rows) whose tokens fit
+one 1024-lane workgroup per CU: each workgroup holds its output vectors and
+writes them once its gathers are done.  Against the oracle, bit-exact, with
+the rows no entry maps to and the output rows of other tokens untouched.
+
+Cases: a last workgroup with fewer tokens (one token), top-k through the
+generic loop (10) and small (2), a small hidden size with many tokens,
+masked entries, unit weights (ep_dispatch_backward), and a batch past the
+one-workgroup-per-CU limit (the other kernel, same bits).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_run import SENT_BF16, host, to_dev
+from workloads import to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def slots(rng, T, K, mask_frac):
+    """Receive rows of (t, k): a random bijection onto T*K rows, with some
+    entries masked (-1)."""
+    s = rng.permutation(T * K).reshape(T, K).astype(np.int32)
+    s[rng.random((T, K)) < mask_frac] = -1
+    return s
+
+
+@pytest.mark.parametrize("T,K,H,mask", [
+    (4001, 8, 7168, 0.05),   # 16 tokens per workgroup, the last one holds one token
+    (500, 10, 7168, 0.0),    # generic top-k loop (8 + 2)
+    (2400, 2, 7168, 0.1),    # K=2
+    (4096, 8, 1024, 0.0),    # 128 work items per token: 2 per lane
+    (3000, 8, 1536, 0.3),    # many masked entries
+])
+@pytest.mark.parametrize("unit", [False, True])
+def test_burst_combine(gpu, T, K, H, mask, unit):
+    ep = gpu
+    assert T * K * H * 2 >= 64 << 20  # the burst path's size
+    rng = np.random.default_rng(T + K + H)
+    s = slots(rng, T, K, mask)
+    y = to_bf16_bits(rng.standard_normal((T * K, H), dtype=np.float32))
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    print("case burst combine T=%d K=%d H=%d unit=%s" % (T, K, H, unit), flush=True)
+    d_s = to_dev(s)
+    d_y = to_dev(y.view(np.int16))
+    out = torch.full((T + 1, H), SENT_BF16, dtype=torch.int16, device="cuda")  # one row past the output
+    if unit:
+        ep.ep_dispatch_backward(d_y, d_s, out[:T])
+        want = oracle.dispatch_backward(y, s)
+    else:
+        ep.ep_combine(d_y, d_s, to_dev(w), out[:T])
+        want = oracle.combine(y, s, w)
+    got = host(out)
+    assert np.array_equal(got[:T], want)
+    assert np.all(got[T] == SENT_BF16)
+
+
+def test_past_one_workgroup_per_cu(gpu):
+    """9000 tokens x 7168: 36 tokens per CU would not fit the held outputs,
+    so the per-item kernel runs; same bits as the oracle."""
+    ep = gpu
+    T, K, H = 9000, 2, 7168
+    rng = np.random.default_rng(9)
+    s = slots(rng, T, K, 0.02)
+    y = to_bf16_bits(rng.standard_normal((T * K, H), dtype=np.float32))
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    print("case combine past the burst limit", flush=True)
+    out = torch.full((T, H), SENT_BF16, dtype=torch.int16, device="cuda")
+    ep.ep_combine(to_dev(y.view(np.int16)), to_dev(s), to_dev(w), out)
+    assert np.array_equal(host(out), oracle.combine(y, s, w))
