@@ -22,12 +22,14 @@
 // hit rows still held in the caches (measured 3.1-3.3 against 3.8 us for
 // 128 tokens, top-8, hidden 7168).  No LDS, no MFMA.
 //
-// Large batches that fit one workgroup per CU (combine_burst_kernel): HBM
-// moves a stream of reads alone faster than one with writes mixed in, so
-// each 1024-lane workgroup owns ceil(T / CUs) consecutive tokens, keeps
-// its finished output vectors in registers (at most kBurstItems per lane)
-// and writes them all once its gathers are done.  The writes of all CUs
-// then come at the end, in one burst, instead of among the reads.
+// Large batches (combine_burst_kernel): HBM moves a stream of reads alone
+// faster than one with writes mixed in, so each 1024-lane workgroup (one
+// per CU) owns ceil(T / CUs) consecutive tokens, keeps its finished output
+// vectors in registers (at most kBurstItems per lane) and writes them all
+// once its gathers are done: the writes of all CUs come at the end, in one
+// burst, instead of among the reads.  A batch with more work items than
+// the workgroups can hold is split into equal slices of tokens, one launch
+// each (T <= 4096 at hidden 7168 is one launch).
 
 // Gathered bytes from which the streaming accesses are used.
 constexpr size_t kStreamingBytes = size_t(64) << 20;
@@ -153,19 +155,6 @@ __global__ __launch_bounds__(kBurstThreads) void combine_burst_kernel(const uint
   }
 }
 
-// CUs of the current device (read once per device).
-int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
-
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w, int32_t T, int32_t H,
@@ -175,26 +164,39 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w
   if (n_items == 0) return hipSuccess;
   const dim3 grid((n_items + kThreads - 1) / kThreads), block(kThreads);
   const bool nt = static_cast<size_t>(T) * K * H * 2 >= kStreamingBytes;
-  // burst: large batches whose tokens fit one workgroup per CU
-  const int cus = nt ? device_cus() : 0;
-  const int tpb = cus > 0 ? (T + cus - 1) / cus : 0;
-  if (tpb > 0 && static_cast<int64_t>(tpb) * vpt <= static_cast<int64_t>(kBurstItems) * kBurstThreads) {
-    const dim3 bgrid((T + tpb - 1) / tpb), bblock(kBurstThreads);
-#define EP_COMBINE_BURST(KV)                                                                                 \
-  if (w == nullptr)                                                                                          \
-    hipLaunchKernelGGL((combine_burst_kernel<KV, true>), bgrid, bblock, 0, stream, y, slot, w, T, H, K, tpb, out); \
-  else                                                                                                       \
-    hipLaunchKernelGGL((combine_burst_kernel<KV, false>), bgrid, bblock, 0, stream, y, slot, w, T, H, K, tpb, out)
-    switch (K) {
-      case 1: { EP_COMBINE_BURST(1); } break;
-      case 2: { EP_COMBINE_BURST(2); } break;
-      case 4: { EP_COMBINE_BURST(4); } break;
-      case 6: { EP_COMBINE_BURST(6); } break;
-      case 8: { EP_COMBINE_BURST(8); } break;
-      default: { EP_COMBINE_BURST(0); } break;
-    }
+  // burst: large batches, one workgroup per CU, in equal token slices of at
+  // most one held round each
+  const int cus = nt ? device_cu_count() : 0;
+  const int tpb_max = static_cast<int>(static_cast<uint32_t>(kBurstItems * kBurstThreads) / vpt);
+  if (cus > 0 && tpb_max > 0) {
+    const int64_t per_launch = static_cast<int64_t>(cus) * tpb_max;
+    const int launches = static_cast<int>((T + per_launch - 1) / per_launch);
+    const int slice = (T + launches - 1) / launches;
+    for (int t0 = 0; t0 < T; t0 += slice) {
+      const int Ts = min(slice, T - t0);
+      const int tpb = (Ts + cus - 1) / cus;
+      const dim3 bgrid((Ts + tpb - 1) / tpb), bblock(kBurstThreads);
+      const int32_t* sl = slot + static_cast<size_t>(t0) * K;
+      const float* ws = w != nullptr ? w + static_cast<size_t>(t0) * K : nullptr;
+      uint16_t* os = out + static_cast<size_t>(t0) * H;
+#define EP_COMBINE_BURST(KV)                                                                                    \
+  if (ws == nullptr)                                                                                            \
+    hipLaunchKernelGGL((combine_burst_kernel<KV, true>), bgrid, bblock, 0, stream, y, sl, ws, Ts, H, K, tpb, os); \
+  else                                                                                                          \
+    hipLaunchKernelGGL((combine_burst_kernel<KV, false>), bgrid, bblock, 0, stream, y, sl, ws, Ts, H, K, tpb, os)
+      switch (K) {
+        case 1: { EP_COMBINE_BURST(1); } break;
+        case 2: { EP_COMBINE_BURST(2); } break;
+        case 4: { EP_COMBINE_BURST(4); } break;
+        case 6: { EP_COMBINE_BURST(6); } break;
+        case 8: { EP_COMBINE_BURST(8); } break;
+        default: { EP_COMBINE_BURST(0); } break;
+      }
 #undef EP_COMBINE_BURST
-    return hipGetLastError();
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
 #define EP_COMBINE_NT(KV, U, NTV) \
   hipLaunchKernelGGL((combine_kernel<KV, U, NTV>), grid, block, 0, stream, y, slot, w, n_items, vpt, H, K, out)

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "ep_internal.h"
 
 #define EP_API extern "C" __attribute__((visibility("default")))
@@ -27,6 +29,8 @@ constexpr int64_t kMaxElems = int64_t(1) << 34;
 constexpr int64_t kMaxCast = int64_t(1) << 33;
 
 ep_status from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+constexpr int kMaxDevices = 64;
 
 ep_status check_common(int64_t T, int32_t K) {
   if (T < 0 || K < 1) return EP_ERR_INVALID_ARG;
@@ -86,6 +90,23 @@ ep_status check_dispatch(const void* x, int64_t T, int32_t H, int32_t K, const f
 }
 
 }  // namespace
+
+namespace ep {
+
+int device_cu_count() {
+  // threads that race to fill an entry all store the same value
+  static std::atomic<int> cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace ep
 
 EP_API const char* ep_status_string(int status) {
   switch (status) {

@@ -59,6 +59,11 @@ bool launch_layout_dispatch_chunked(const Idx* topk_idx, const uint16_t* x, cons
                                     int32_t* src, void* recv, float* recv_scale, float* recv_weight,
                                     hipStream_t stream, hipError_t* err);
 
+// Compute units of the current device (read once per device; 0 if the
+// runtime cannot tell).  Kernels that size their grid at one workgroup per
+// CU take it from here, so a partitioned GPU gets a grid that fits it.
+int device_cu_count();
+
 // Dispatch reads the tokens with non-temporal loads from this many bytes of
 // tokens on (they are read once); smaller batches are usually still cached.
 constexpr size_t kStreamingTokenBytes = size_t(16) << 20;

@@ -27,7 +27,6 @@ namespace ep {
 namespace {
 
 constexpr int kMaxItems = 8;       // work items per thread (token loads held in registers)
-constexpr int kTargetGroups = 256;  // about one workgroup per CU of an MI355X
 constexpr int kChunkMaxK = 64;      // one lane per row for the wavefront scale stores
 
 // FP8: work item = (token, 16 channels) as in the dispatch kernel; BF16:
@@ -140,7 +139,9 @@ bool launch_layout_dispatch_chunked(const Idx* topk_idx, const uint16_t* x, cons
   const int per16 = 16 / static_cast<int>(sizeof(Idx));
   int step = 1;
   while (v4 && (step * K) % per16 != 0) ++step;
-  int tpb = (T + kTargetGroups - 1) / kTargetGroups;
+  const int cus = device_cu_count();  // one workgroup per CU
+  if (cus <= 0) return false;
+  int tpb = (T + cus - 1) / cus;
   tpb = (tpb + step - 1) / step * step;
   if (tpb * K > threads || static_cast<int64_t>(tpb) * vpt > static_cast<int64_t>(kMaxItems) * threads) return false;
   const size_t lds = chunk_lds_bytes(nw, E) + static_cast<size_t>(tpb) * K * sizeof(int);

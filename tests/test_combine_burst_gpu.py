@@ -1,12 +1,13 @@
-"""Combine of large batches (from 64 MB of gathered rows) whose tokens fit
-one 1024-lane workgroup per CU: each workgroup holds its output vectors and
-writes them once its gathers are done.  Against the oracle, bit-exact, with
-the rows no entry maps to and the output rows of other tokens untouched.
+"""Combine of large batches (from 64 MB of gathered rows): each 1024-lane
+workgroup (one per CU) holds up to 14 output vectors per lane and writes
+them once their gathers are done; larger batches go as equal token slices,
+one launch each.  Against the oracle, bit-exact, with the output rows of
+other tokens untouched.
 
 Cases: a last workgroup with fewer tokens (one token), top-k through the
 generic loop (10) and small (2), a small hidden size with many tokens,
-masked entries, unit weights (ep_dispatch_backward), and a batch past the
-one-workgroup-per-CU limit (the other kernel, same bits).
+masked entries, unit weights (ep_dispatch_backward), and batches split
+into several launches.
 """
 
 import numpy as np
@@ -58,16 +59,17 @@ def test_burst_combine(gpu, T, K, H, mask, unit):
     assert np.all(got[T] == SENT_BF16)
 
 
-def test_past_one_workgroup_per_cu(gpu):
-    """9000 tokens x 7168: 36 tokens per CU would not fit the held outputs,
-    so the per-item kernel runs; same bits as the oracle."""
+@pytest.mark.parametrize("T,K,H", [(9000, 2, 7168), (8192, 8, 7168)])
+def test_several_launches(gpu, T, K, H):
+    """More tokens than 256 workgroups can hold at hidden 7168 (16 each):
+    9000 tokens go as three launches of 3000 (12 tokens per workgroup),
+    8192 as two of 4096."""
     ep = gpu
-    T, K, H = 9000, 2, 7168
-    rng = np.random.default_rng(9)
+    rng = np.random.default_rng(T + K)
     s = slots(rng, T, K, 0.02)
     y = to_bf16_bits(rng.standard_normal((T * K, H), dtype=np.float32))
     w = rng.standard_normal((T, K)).astype(np.float32)
-    print("case combine past the burst limit", flush=True)
+    print("case burst combine launches T=%d K=%d" % (T, K), flush=True)
     out = torch.full((T, H), SENT_BF16, dtype=torch.int16, device="cuda")
     ep.ep_combine(to_dev(y.view(np.int16)), to_dev(s), to_dev(w), out)
     assert np.array_equal(host(out), oracle.combine(y, s, w))
