@@ -257,10 +257,11 @@ hipError_t launch_layout(const Idx* topk_idx, int32_t rows, int32_t top_k, int32
                      counts, offsets, slot, src)
 #define EP_LAYOUT_FUSED(NW) \
   if (v4) EP_LAYOUT_FUSED_V(NW, true); else EP_LAYOUT_FUSED_V(NW, false)
-    if (nw >= 16) { EP_LAYOUT_FUSED(16); }
-    else if (nw >= 8) { EP_LAYOUT_FUSED(8); }
-    else if (nw >= 4) { EP_LAYOUT_FUSED(4); }
-    else { EP_LAYOUT_FUSED(1); }
+    // the kernel's NW must equal the launched waves; up to EP_MAX_EXPERTS
+    // (1024) experts chunk_waves gives 16 or 8
+    if (nw == 16) { EP_LAYOUT_FUSED(16); }
+    else if (nw == 8) { EP_LAYOUT_FUSED(8); }
+    else { return hipErrorInvalidValue; }
 #undef EP_LAYOUT_FUSED
 #undef EP_LAYOUT_FUSED_V
     return hipGetLastError();
