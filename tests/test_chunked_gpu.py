@@ -133,6 +133,9 @@ def test_skewed_prefill(gpu):
     (1500, 8, 256, 7168, 128, 0.0),  # padded, full hidden size
     (4100, 1, 16, 128, 0, 0.5),      # half the entries masked
     (500, 16, 8, 640, 0, 0.0),       # K=16 over 8 experts: repeated experts in a token
+    (200, 32, 64, 1024, 0, 0.05),    # K at its maximum: one token per workgroup
+    (2000, 3, 256, 1152, 0, 0.05),   # odd K: 8 tokens per workgroup for 16-byte id loads
+    (1025, 3, 64, 2048, 0, 0.0),     # odd K, the last workgroup holds one token
 ])
 def test_shapes(gpu, T, K, E, H, cap, mask):
     rng = np.random.default_rng(T * 7919 + K * 31 + E + H)
@@ -146,15 +149,17 @@ def test_shapes(gpu, T, K, E, H, cap, mask):
 
 @pytest.mark.parametrize("dtype", [np.int32, np.int64])
 @pytest.mark.parametrize("id_offset", [0, 1])
-def test_id_widths_and_alignment(gpu, dtype, id_offset):
+@pytest.mark.parametrize("K", [8, 5])
+def test_id_widths_and_alignment(gpu, dtype, id_offset, K):
     """16-byte id loads when the ids are 16-byte aligned, else element loads;
-    int64 ids that wrap in 32 bits stay masked."""
-    rng = np.random.default_rng(77 + id_offset + (dtype == np.int64))
-    T, K, E, H = 1800, 8, 256, 1024
+    int64 ids that wrap in 32 bits stay masked; odd K makes the chunk size
+    a multiple of 4 (int32) or 2 (int64) ids only by the token count."""
+    rng = np.random.default_rng(77 + id_offset + (dtype == np.int64) + K)
+    T, E, H = 1800, 256, 1024
     idx = routing(rng, T, K, E, mask_frac=0.05, dtype=dtype)
     x = tokens(rng, T, H)
     w = rng.standard_normal((T, K)).astype(np.float32)
-    print("case chunked ids %s offset=%d" % (np.dtype(dtype).name, id_offset), flush=True)
+    print("case chunked ids %s offset=%d K=%d" % (np.dtype(dtype).name, id_offset, K), flush=True)
     run_and_check(gpu, idx, x, w, E, 0, True, id_offset=id_offset)
     run_and_check(gpu, idx, x, w, E, 16, True, id_offset=id_offset)
 

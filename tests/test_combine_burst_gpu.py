@@ -73,3 +73,21 @@ def test_several_launches(gpu, T, K, H):
     out = torch.full((T, H), SENT_BF16, dtype=torch.int16, device="cuda")
     ep.ep_combine(to_dev(y.view(np.int16)), to_dev(s), to_dev(w), out)
     assert np.array_equal(host(out), oracle.combine(y, s, w))
+
+
+@pytest.mark.parametrize("T,K,H", [
+    (131072, 32, 8),     # H = 8: one work item per token, a wavefront spans 64 tokens (T*K at its 2^22 limit)
+    (64, 32, 16384),     # fewer tokens than CUs: one token per workgroup
+    (37, 8, 114696),     # 14337 work items per token, more than a lane can hold: the per-item kernel
+])
+def test_extreme_shapes(gpu, T, K, H):
+    ep = gpu
+    assert T * K * H * 2 >= 64 << 20
+    rng = np.random.default_rng(T + K + H)
+    s = slots(rng, T, K, 0.05)
+    y = to_bf16_bits(rng.standard_normal((T * K, H), dtype=np.float32))
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    print("case burst combine extreme T=%d K=%d H=%d" % (T, K, H), flush=True)
+    out = torch.full((T, H), SENT_BF16, dtype=torch.int16, device="cuda")
+    ep.ep_combine(to_dev(y.view(np.int16)), to_dev(s), to_dev(w), out)
+    assert np.array_equal(host(out), oracle.combine(y, s, w))
