@@ -236,7 +236,7 @@ ep_status ep_layout_dispatch_i64(const int64_t* topk_idx, const void* x, const f
  * topk_weights float32 [T, K]
  * out          bf16 bits [T, H] out, 16-byte aligned; must not overlap y
  * Requirements: H > 0, H % 8 == 0, 1 <= K <= EP_MAX_TOPK, T*K <= 2^22,
- * T*H < 2^35.
+ * T*H < 2^34.
  */
 ep_status ep_combine(const void* y, const int32_t* slot, const float* topk_weights,
                      int64_t num_tokens, int32_t hidden, int32_t top_k, void* out,
