@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name,capacity,fused", [("decode", 0, False), ("decode", 128, False), ("prefill", 0, False),
-                                                ("decode", 0, True), ("decode", 128, True)])
+                                                ("decode", 0, True), ("decode", 128, True), ("prefill", 0, True)])
 def test_graph_replays_match_eager(gpu, name, capacity, fused):
     """fused: layout and dispatch through the one ep_layout_dispatch call."""
     ep = gpu
