@@ -20,19 +20,35 @@
 // Against the layout kernel followed by the dispatch kernel this saves the
 // second launch and hides the layout's on-chip work under the token reads.
 
+#include <type_traits>
+
 #include "ep_internal.h"
 #include "layout_device.h"
 
 namespace ep {
 namespace {
 
-constexpr int kMaxItems = 8;       // work items per thread (token loads held in registers)
+// work items per thread, their token loads held in registers (two 16-byte
+// loads per FP8 item, one per BF16 item: 64 and 56 VGPRs; 14 BF16 items
+// hold 16 tokens of hidden 7168, and 16 would spill)
+constexpr int max_items(bool fp8) { return fp8 ? 8 : 14; }
 constexpr int kChunkMaxK = 64;      // one lane per row for the wavefront scale stores
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled by construction:
+// the token registers a[I], b[I] must be indexed by constants (an index the
+// compiler does not resolve puts the arrays in scratch memory).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // FP8: work item = (token, 16 channels) as in the dispatch kernel; BF16:
 // (token, 8 channels).  NT: non-temporal token loads and scale stores; WS:
 // wavefront scale stores (store_wave_scales).  Each thread holds the work
-// items i*kThreads + tid, i < kMaxItems, of its workgroup's tokens.
+// items i*kThreads + tid, i < max_items(FP8), of its workgroup's tokens.
 template <int NW, bool V4, typename Idx, bool FP8, bool NT, bool WS>
 __global__ __launch_bounds__(NW * kWave) void layout_dispatch_chunked(
     const Idx* __restrict__ idx, const uint16_t* __restrict__ x, const float* __restrict__ w, int32_t T,
@@ -49,27 +65,33 @@ __global__ __launch_bounds__(NW * kWave) void layout_dispatch_chunked(
   const uint32_t nitems = static_cast<uint32_t>(ntok) * vpt;
   const int nit = static_cast<int>((nitems + kThreads - 1) / kThreads);  // workgroup-uniform
 
-  // Token loads: all kMaxItems item slots are loaded, with no branch (item
-  // slots past the last item load a copy of it, from the cache, and store
-  // nothing).  Item 0 goes out once the ids are in, items 1.. one per step
-  // of the histogram: HBM takes the tokens no faster than it reads them,
-  // so loads issued all at once stall their waves for the whole read,
-  // while loads spread over the histogram keep HBM busy under the counting.
-  static_assert(kMaxItems <= kChunkSteps + 1, "every item load has a hook");
-  u32x4 a[kMaxItems], b[kMaxItems];
+  // Token loads: the item slots up to the workgroup's last item are
+  // loaded, with no per-lane branch (slots past a lane's last item load a
+  // copy of the workgroup's last item, from the cache, and store nothing).  Item 0 goes out once the ids are in, the others spread over
+  // the steps of the histogram (one FP8 item or two BF16 items per step):
+  // HBM takes the tokens no faster than it reads them, so loads issued all
+  // at once stall their waves for the whole read, while loads spread over
+  // the histogram keep HBM busy under the counting.
+  constexpr int kItems = max_items(FP8);
+  constexpr int kPerStep = FP8 ? 1 : 2;
+  static_assert(kItems <= 1 + kPerStep * kChunkSteps, "every item load has a hook");
+  u32x4 a[kItems], b[FP8 ? kItems : 1];
   auto load_item = [&](int i) {
+    if (i >= nit) return;  // workgroup-uniform: no slot of this one holds an item
     const uint32_t item = min(static_cast<uint32_t>(i * kThreads + tid), nitems - 1);
     const uint32_t tl = item / vpt, v = item - tl * vpt;
     const u32x4* p = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(tok0 + tl) * H) + (FP8 ? 2 * v : v);
     a[i] = load_token<NT>(p);
-    if (FP8) b[i] = load_token<NT>(p + 1);
+    if constexpr (FP8) b[i] = load_token<NT>(p + 1);
   };
   // 16 ids per thread at a time with int64 ids (8 loads, as with int32): the
   // token registers and 16 id loads would not fit in 128 VGPRs
   const int row = layout_chunk<NW, V4, Idx, true, sizeof(Idx) == 8 ? 16 : 32>(
       idx, T * K, K, E, cap, c0, c1, lds64, counts, offsets, slot, src, [&] { load_item(0); },
       [&](int u) {
-        if (u + 1 < kMaxItems) load_item(u + 1);
+#pragma unroll
+        for (int j = 0; j < kPerStep; ++j)
+          if (1 + kPerStep * u + j < kItems) load_item(1 + kPerStep * u + j);
       });
 
   int* rows = reinterpret_cast<int*>(reinterpret_cast<char*>(lds64) + chunk_lds_bytes(NW, E));  // [tpb*K]
@@ -77,9 +99,9 @@ __global__ __launch_bounds__(NW * kWave) void layout_dispatch_chunked(
   __syncthreads();
 
   const uint32_t G = static_cast<uint32_t>(H) / kGroup;
-#pragma unroll
-  for (int i = 0; i < kMaxItems; ++i) {
-    if (i >= nit) break;
+  static_for<0, kItems>([&](auto ic_) {
+    constexpr int i = decltype(ic_)::value;
+    if (i >= nit) return;
     const uint32_t item = static_cast<uint32_t>(i * kThreads + tid);
     const bool active = item < nitems;  // with WS whole wavefronts only
     const uint32_t ic = active ? item : nitems - 1;
@@ -108,7 +130,7 @@ __global__ __launch_bounds__(NW * kWave) void layout_dispatch_chunked(
       }
       if (WS) store_wave_scales<NT>(rj, s, v, G, recv_scale);
     } else {
-      if (!active) continue;
+      if (!active) return;
       uint16_t* out = static_cast<uint16_t*>(recv);
       for (int k = 0; k < K; ++k) {
         const int r = trow[k];
@@ -117,7 +139,7 @@ __global__ __launch_bounds__(NW * kWave) void layout_dispatch_chunked(
         if (want_w) recv_weight[r] = wrow[k];
       }
     }
-  }
+  });
 }
 
 }  // namespace
@@ -143,7 +165,8 @@ bool launch_layout_dispatch_chunked(const Idx* topk_idx, const uint16_t* x, cons
   if (cus <= 0) return false;
   int tpb = (T + cus - 1) / cus;
   tpb = (tpb + step - 1) / step * step;
-  if (tpb * K > threads || static_cast<int64_t>(tpb) * vpt > static_cast<int64_t>(kMaxItems) * threads) return false;
+  if (tpb * K > threads || static_cast<int64_t>(tpb) * vpt > static_cast<int64_t>(max_items(fp8)) * threads)
+    return false;
   const size_t lds = chunk_lds_bytes(nw, E) + static_cast<size_t>(tpb) * K * sizeof(int);
   if (lds > kLdsLimit) return false;
   const bool nt = static_cast<size_t>(T) * H * 2 >= kStreamingTokenBytes;
