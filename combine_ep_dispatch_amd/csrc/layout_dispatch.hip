@@ -13,12 +13,12 @@
 // tokens b*tpb .. b*tpb+tpb-1: their K*tpb entries are its layout chunk,
 // and it also dispatches those tokens.  The tokens' loads are spread over
 // the steps of the histogram (which is bound by on-chip work), and once
-// the chunk's rows are known (staged in LDS) the workgroup quantises the
-// tokens and writes its receive rows.  tpb
-// is chosen so that there is about one workgroup per CU: the histogram is
-// then paid once per CU, and the dispatch stores still come from every CU.
-// Against the layout kernel followed by the dispatch kernel this saves the
-// second launch and hides the layout's on-chip work under the token reads.
+// the chunk's rows are known (staged in LDS) the workgroup quantises (FP8)
+// or copies (BF16) the tokens into its receive rows.  tpb is chosen so
+// that there is one workgroup per CU: the histogram is then paid once per
+// CU, and the dispatch stores still come from every CU.  Against the
+// layout kernel followed by the dispatch kernel this saves the second
+// launch and hides the layout's on-chip work under the token reads.
 
 #include <type_traits>
 
@@ -32,7 +32,7 @@ namespace {
 // loads per FP8 item, one per BF16 item: 64 and 56 VGPRs; 14 BF16 items
 // hold 16 tokens of hidden 7168, and 16 would spill)
 constexpr int max_items(bool fp8) { return fp8 ? 8 : 14; }
-constexpr int kChunkMaxK = 64;      // one lane per row for the wavefront scale stores
+constexpr int kChunkMaxK = 64;  // one lane per row for the wavefront scale stores
 
 // f(integral_constant<int, I>) for I = 0 .. N-1, unrolled by construction:
 // the token registers a[I], b[I] must be indexed by constants (an index the
