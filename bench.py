@@ -458,6 +458,7 @@ def summarize_profile(dirname):
              ("combine_kernel<8, true,", d_bwd),  # ep_dispatch_backward
              ("combine_burst_kernel<8, true>", d_bwd),
              ("grad_rows_kernel", 2 * T * H + 8 * T * K + 2 * T * K * H),
+             ("fanout_burst_bf16<true", 2 * T * H + 8 * T * K + 2 * T * K * H),  # the same, as a burst
              ("grad_weights_kernel", 2 * T * H + 2 * T * K * H + 8 * T * K))
     for prefix, a in known:
         for kern in sorted({k for (k, c) in avg if k.startswith(prefix)}):

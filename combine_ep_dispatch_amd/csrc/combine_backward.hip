@@ -187,9 +187,13 @@ hipError_t launch_combine_backward(const uint16_t* grad_out, const uint16_t* y, 
   const dim3 rgrid((n_items + kRowThreads - 1) / kRowThreads), rblock(kRowThreads);
   const int lanes = (H / 8 + kWave - 1) / kWave * kWave;
   const dim3 wgrid(T), wblock(lanes);
+  hipError_t e = hipSuccess;
+  const bool burst = launch_fanout_burst_bf16(grad_out, slot, w, T, H, K, true, grad_y, nullptr, stream, &e);
+  if (e != hipSuccess) return e;
 #define EP_COMBINE_BWD(KV)                                                                                    \
-  hipLaunchKernelGGL(grad_rows_kernel<KV>, rgrid, rblock, 0, stream, grad_out, slot, w, n_items, vpt, H, K,   \
-                     grad_y);                                                                                 \
+  if (!burst)                                                                                                 \
+    hipLaunchKernelGGL(grad_rows_kernel<KV>, rgrid, rblock, 0, stream, grad_out, slot, w, n_items, vpt, H, K, \
+                       grad_y);                                                                               \
   if (grad_w != nullptr)                                                                                      \
     hipLaunchKernelGGL(grad_weights_kernel<KV>, wgrid, wblock, 0, stream, grad_out, y, slot, H, K, grad_w)
   switch (K) {

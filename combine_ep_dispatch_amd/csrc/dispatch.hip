@@ -139,6 +139,72 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
   }
 }
 
+// Burst fan-out of BF16 token rows (the BF16 dispatch, and the combine
+// backward's row gradients): HBM writes faster when no reads are mixed in,
+// so each 1024-lane workgroup (one per CU) owns tpb consecutive tokens,
+// loads all its work items (token, 8 channels) first, up to kFanItems per
+// lane, with the tokens' K receive rows (and weights) staged in LDS, and
+// then writes the K copies.  WEIGHTED: copy k is BF16_RNE(RN32(w[t,k] *
+// x[t,c])) per channel; else the bits unchanged, with recv_weight[r] =
+// w[t,k] when recv_weight is given.
+constexpr int kFanThreads = 1024;
+constexpr int kFanItems = 14;  // token vectors held per lane (4 VGPRs each)
+
+template <bool WEIGHTED, bool NT>
+__global__ __launch_bounds__(kFanThreads) void fanout_burst_bf16(const uint16_t* __restrict__ x,
+                                                                 const int32_t* __restrict__ slot,
+                                                                 const float* __restrict__ w, int32_t T, int32_t H,
+                                                                 int32_t K, int32_t tpb, uint16_t* __restrict__ out,
+                                                                 float* __restrict__ recv_weight) {
+  extern __shared__ int32_t fan_lds[];  // rows [tpb*K], then weights [tpb*K]
+  const int tid = threadIdx.x;
+  const int tok0 = blockIdx.x * tpb;
+  const int ntok = min(T - tok0, tpb);
+  const uint32_t vpt = static_cast<uint32_t>(H) / 8;
+  const uint32_t nitems = static_cast<uint32_t>(ntok) * vpt;
+  const int nit = static_cast<int>((nitems + kFanThreads - 1) / kFanThreads);  // workgroup-uniform
+  u32x4 d[kFanItems];
+  static_for<0, kFanItems>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if (i >= nit) return;
+    const uint32_t item = min(static_cast<uint32_t>(i * kFanThreads + tid), nitems - 1);
+    const uint32_t tl = item / vpt;
+    d[i] = load_token<NT>(reinterpret_cast<const u32x4*>(x + static_cast<size_t>(tok0 + tl) * H) + (item - tl * vpt));
+  });
+  const bool need_w = WEIGHTED || recv_weight != nullptr;
+  int32_t* rows = fan_lds;
+  float* wts = reinterpret_cast<float*>(fan_lds + tpb * K);
+  for (int e = tid; e < ntok * K; e += kFanThreads) {
+    rows[e] = slot[static_cast<size_t>(tok0) * K + e];
+    if (need_w) wts[e] = w[static_cast<size_t>(tok0) * K + e];
+  }
+  __syncthreads();
+  static_for<0, kFanItems>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const uint32_t item = static_cast<uint32_t>(i * kFanThreads + tid);
+    if (i >= nit || item >= nitems) return;
+    const uint32_t tl = item / vpt, v = item - tl * vpt;
+    const int32_t* tr = rows + tl * K;
+    const float* tw = wts + tl * K;
+    for (int k = 0; k < K; ++k) {
+      const int r = tr[k];
+      if (r < 0) continue;
+      u32x4* dst = reinterpret_cast<u32x4*>(out + static_cast<size_t>(r) * H) + v;
+      if constexpr (WEIGHTED) {
+        const float wk = tw[k];
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = f32_to_bf16_rne(__fmul_rn(wk, bf16_lo(d[i][q]))) | (f32_to_bf16_rne(__fmul_rn(wk, bf16_hi(d[i][q]))) << 16);
+        *dst = o;
+      } else {
+        *dst = d[i];
+        if (recv_weight != nullptr && v == 0) recv_weight[r] = tw[k];
+      }
+    }
+  });
+}
+
 __global__ __launch_bounds__(kThreads) void cast_fp8_kernel(const float* __restrict__ in,
                                                             uint8_t* __restrict__ out, int64_t n) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
@@ -188,8 +254,43 @@ hipError_t launch_dispatch_fp8(const uint16_t* x, int32_t T, int32_t H, int32_t 
   return hipGetLastError();
 }
 
+bool launch_fanout_burst_bf16(const uint16_t* x, const int32_t* slot, const float* w, int32_t T, int32_t H,
+                              int32_t K, bool weighted, uint16_t* out, float* recv_weight, hipStream_t stream,
+                              hipError_t* err) {
+  // tokens of 16 MB and more (read once, non-temporal), one workgroup per
+  // CU, in equal token slices of at most kFanItems vectors per lane each
+  if (static_cast<size_t>(T) * H * 2 < kStreamingTokenBytes) return false;
+  const int cus = device_cu_count();
+  const int vpt = H / 8;
+  const int tpb_max = kFanItems * kFanThreads / vpt;
+  if (cus <= 0 || tpb_max <= 0) return false;
+  const int64_t per_launch = static_cast<int64_t>(cus) * tpb_max;
+  const int launches = static_cast<int>((T + per_launch - 1) / per_launch);
+  const int slice = (T + launches - 1) / launches;
+  for (int t0 = 0; t0 < T; t0 += slice) {
+    const int Ts = min(slice, T - t0);
+    const int tpb = (Ts + cus - 1) / cus;
+    const dim3 grid((Ts + tpb - 1) / tpb), block(kFanThreads);
+    const size_t lds = static_cast<size_t>(tpb) * K * 8;
+    const int32_t* sl = slot + static_cast<size_t>(t0) * K;
+    const float* ws = w != nullptr ? w + static_cast<size_t>(t0) * K : nullptr;
+    const uint16_t* xs = x + static_cast<size_t>(t0) * H;
+    if (weighted)
+      hipLaunchKernelGGL((fanout_burst_bf16<true, true>), grid, block, lds, stream, xs, sl, ws, Ts, H, K, tpb, out,
+                         nullptr);
+    else
+      hipLaunchKernelGGL((fanout_burst_bf16<false, true>), grid, block, lds, stream, xs, sl, ws, Ts, H, K, tpb, out,
+                         recv_weight);
+    *err = hipGetLastError();
+    if (*err != hipSuccess) return true;
+  }
+  return true;
+}
+
 hipError_t launch_dispatch_bf16(const uint16_t* x, int32_t T, int32_t H, int32_t K, const int32_t* slot,
                                 const float* w, uint16_t* recv, float* recv_weight, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (launch_fanout_burst_bf16(x, slot, w, T, H, K, false, recv, recv_weight, stream, &e)) return e;
   const uint32_t vpt = static_cast<uint32_t>(H) / 8;
   const uint32_t n_items = static_cast<uint32_t>(T) * vpt;
   if (n_items == 0) return hipSuccess;

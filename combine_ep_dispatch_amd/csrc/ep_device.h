@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ep {
 
 constexpr int kWave = 64;
@@ -169,6 +171,18 @@ __device__ __forceinline__ u32x4 quantize16_e4m3(u32x4 a, u32x4 b, float& scale)
     q[j] = f32x4_to_e4m3(f[4 * j] / s, f[4 * j + 1] / s, f[4 * j + 2] / s, f[4 * j + 3] / s);
   scale = s;
   return q;
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled by construction:
+// registers held in arrays (a lane's token vectors) must be indexed by
+// constants, and an index the compiler does not resolve puts the array in
+// scratch memory (`#pragma unroll` is only a request).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 // ---- dispatch stores ------------------------------------------------------

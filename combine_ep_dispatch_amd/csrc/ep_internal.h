@@ -27,6 +27,13 @@ hipError_t launch_dispatch_bf16(const uint16_t* x, int32_t num_tokens, int32_t h
                                 const int32_t* slot, const float* topk_weights, uint16_t* recv,
                                 float* recv_weight, hipStream_t stream);
 
+// The burst fan-out of BF16 token rows (from 16 MB of tokens): out[slot[t,k]]
+// = x[t] (weighted: BF16_RNE(RN32(w[t,k] * x[t])) per channel); returns false,
+// launching nothing, below its size or where the device's CU count is unknown.
+bool launch_fanout_burst_bf16(const uint16_t* x, const int32_t* slot, const float* w, int32_t T, int32_t H,
+                              int32_t K, bool weighted, uint16_t* out, float* recv_weight, hipStream_t stream,
+                              hipError_t* err);
+
 // topk_weights == nullptr: unit weights (the backward of dispatch)
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* topk_weights,
                           int32_t num_tokens, int32_t hidden, int32_t top_k, uint16_t* out,

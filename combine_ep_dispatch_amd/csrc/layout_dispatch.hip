@@ -20,8 +20,6 @@
 // layout kernel followed by the dispatch kernel this saves the second
 // launch and hides the layout's on-chip work under the token reads.
 
-#include <type_traits>
-
 #include "ep_internal.h"
 #include "layout_device.h"
 
@@ -33,17 +31,6 @@ namespace {
 // hold 16 tokens of hidden 7168, and 16 would spill)
 constexpr int max_items(bool fp8) { return fp8 ? 8 : 14; }
 constexpr int kChunkMaxK = 64;  // one lane per row for the wavefront scale stores
-
-// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled by construction:
-// the token registers a[I], b[I] must be indexed by constants (an index the
-// compiler does not resolve puts the arrays in scratch memory).
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
 
 // FP8: work item = (token, 16 channels) as in the dispatch kernel; BF16:
 // (token, 8 channels).  NT: non-temporal token loads and scale stores; WS:
