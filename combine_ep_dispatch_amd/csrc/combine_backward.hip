@@ -5,11 +5,14 @@
 // combine computes out[t] = sum_k w[t,k] * y[slot[t,k]], so
 //   grad_y[slot[t,k], c] = BF16_RNE(RN32(w[t,k] * grad_out[t,c]))
 //   grad_w[t,k]          = sum_c grad_out[t,c] * y[slot[t,k], c]
-// The dot product has a fixed order, so results are reproducible and
-// bit-identical to the definition: the 8 products of each 8-channel vector
-// are added in channel order into +0.0, then the H/8 vector sums are added
-// as a complete binary tree of adjacent pairs, padded with -0.0 (an exact
-// identity for addition).
+// The dot product has a fixed order, so results are reproducible run to
+// run: the 8 products of each 8-channel vector (exact: BF16 x BF16 fits
+// binary32) are added in channel order into +0.0, then the H/8 vector sums
+// are added as a complete binary tree of adjacent pairs, padded with -0.0
+// (an exact identity for addition).  Each product thus passes through at
+// most 7 + ceil(log2(H/8)) rounded additions, which bounds the distance
+// to the exact dot product by that many units of 2^-24 times
+// sum |grad_out * y| (recursive summation error).
 //
 // gfx950 design: two HBM-bound kernels, which on MI355X measured ~13%
 // faster than one kernel doing both (the reads then run without the

@@ -262,9 +262,14 @@ ep_status ep_dispatch_backward(const void* grad_recv, const int32_t* slot, int64
  * and the routing weights ([P5 "典型工作流程"], backward helpers):
  *   grad_y[slot[t,k], c] = BF16_RNE(RN32(topk_weights[t,k] * grad_out[t,c]))
  *   grad_w[t,k] = sum_c grad_out[t,c] * y[slot[t,k], c]      (binary32)
- * The dot product has a fixed order: the 8 products of each 8-channel
- * vector are added in channel order into +0.0, then the H/8 vector sums are
- * added as a complete binary tree of adjacent pairs padded with -0.0.
+ * Every product of two BF16 values is exact in binary32; the sum is taken
+ * in a fixed order (so results are reproducible run to run), in which
+ * each product passes through at most 7 + ceil(log2(H/8)) rounded binary32
+ * additions: the 8 products of each 8-channel vector are added in channel
+ * order into +0.0, then the H/8 vector sums as a binary tree.  grad_w is
+ * therefore within (7 + ceil(log2(H/8))) * 2^-24 * (1 + 2^-16) *
+ * sum_c |grad_out[t,c] * y[slot[t,k], c]| of the exact dot product (plus
+ * H * 2^-150 where products fall below the normal binary32 range).
  * Masked entries get grad_w = +0.0 and no grad_y row; other grad_y rows are
  * left untouched.
  * grad_out bf16 [T, H]; y bf16 [rows, H] (may be NULL when grad_w is NULL);

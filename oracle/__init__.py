@@ -55,5 +55,5 @@ from .ep_oracle import (  # noqa: F401
     dequantize_rows,
     dispatch_backward,
     combine_backward,
-    pairwise_sum_f32,
+    dot_rn32,
 )

@@ -9,6 +9,8 @@ Terminology: T tokens, H hidden channels, E experts, K experts per token
 (top-k), R = T*K receive rows, G = H/128 scale groups per row.
 """
 
+import math
+
 import numpy as np
 
 from .codecs import bf16_bits_to_f32, f32_to_bf16_rne, f32_to_e4m3_rne_sat, e4m3_to_f32
@@ -248,9 +250,6 @@ def dequantize_rows(recv, recv_scale):
 # functions for training.  The pages give no arithmetic for them; the
 # readings below follow the forward definitions.
 
-VEC = 8  # channels per partial sum of a row dot product
-
-
 def dispatch_backward(grad_recv_bits, slot):
     """Gradient of dispatch w.r.t. x: the K copies' gradients summed.
 
@@ -262,23 +261,32 @@ def dispatch_backward(grad_recv_bits, slot):
     return combine(grad_recv_bits, slot, np.ones(slot.shape, dtype=np.float32))
 
 
-def pairwise_sum_f32(parts):
-    """Sum the last axis of float32 ``parts`` as a complete binary tree of
-    adjacent pairs (leaf i meets leaf i^1 first, then pairs of pairs, ...),
-    after padding the axis to a power of two with -0.0 (x + -0.0 == x for
-    every x, so padding never changes a value)."""
-    a = np.asarray(parts, dtype=np.float32)
-    n = a.shape[-1]
-    m = 1
-    while m < n:
-        m *= 2
-    if m > n:
-        pad = np.full(a.shape[:-1] + (m - n,), -0.0, dtype=np.float32)
-        a = np.concatenate([a, pad], axis=-1)
-    while a.shape[-1] > 1:
-        a = a.reshape(a.shape[:-1] + (a.shape[-1] // 2, 2))
-        a = (a[..., 0] + a[..., 1]).astype(np.float32)
-    return a[..., 0]
+def dot_rn32(a, b):
+    """The dot product of two BF16-valued vectors, rounded once to binary32.
+
+    Every product of two BF16 values is exact in binary64 (8-bit
+    significands give a 16-bit product, far inside binary64's range), and
+    math.fsum returns the binary64 value nearest the exact sum of its
+    terms.  Rounding that to binary32 is a second rounding, which differs
+    from rounding the exact sum only where the binary64 value lies exactly
+    halfway between two binary32 values while the exact sum does not; the
+    sign of the exact remainder (another fsum) then picks the neighbour.
+    An exact zero sum is +0.0.
+    """
+    p = (np.asarray(a, dtype=np.float64) * np.asarray(b, dtype=np.float64)).tolist()
+    s = math.fsum(p)
+    if s == 0.0:
+        return np.float32(0.0)
+    r = np.float32(s)
+    lo = r if float(r) <= s else np.nextafter(r, np.float32(-np.inf))
+    hi = np.nextafter(lo, np.float32(np.inf))
+    if (float(lo) + float(hi)) / 2.0 == s:  # a binary32 midpoint: the exact remainder decides
+        rem = math.fsum(p + [-s])
+        if rem > 0:
+            r = hi
+        elif rem < 0:
+            r = lo
+    return np.float32(r)
 
 
 def combine_backward(grad_out_bits, y_bits, slot, topk_weights, num_rows=None):
@@ -286,13 +294,13 @@ def combine_backward(grad_out_bits, y_bits, slot, topk_weights, num_rows=None):
 
     combine computes out[t] = sum_k w[t,k] * y[slot[t,k]], so
       grad_y[slot[t,k], c] = BF16_RNE(RN32(w[t,k] * grad_out[t,c]))
-      grad_w[t,k]          = sum_c grad_out[t,c] * y[slot[t,k], c]
-    The dot product is given a fixed order so that it is reproducible: each
-    8-channel vector's products are added in channel order into +0.0, then
-    the H/8 vector sums are added as a pairwise tree (``pairwise_sum_f32``).
-    Masked entries (slot -1) get grad_w = +0.0 and no grad_y row; grad_y
-    rows no entry maps to are returned as zeros (the GPU leaves them
-    untouched).
+      grad_w[t,k]          = RN32(sum_c grad_out[t,c] * y[slot[t,k], c])
+    grad_y is the forward product rounded as combine rounds its products,
+    then to BF16 like every row the library writes.  grad_w is the dot
+    product itself, exact and rounded once to binary32 (``dot_rn32``): the
+    pages fix no order for it, so the oracle takes none.  Masked entries
+    (slot -1) get grad_w = +0.0 and no grad_y row; grad_y rows no entry
+    maps to are returned as zeros (the GPU leaves them untouched).
 
     Returns (grad_y uint16[num_rows, H], grad_w float32[T, K]).
     """
@@ -310,9 +318,8 @@ def combine_backward(grad_out_bits, y_bits, slot, topk_weights, num_rows=None):
         m = r >= 0
         gy = (w[m, k][:, None] * g[m]).astype(np.float32)
         grad_y[r[m]] = f32_to_bf16_rne(gy)
-        prod = (g[m] * bf16_bits_to_f32(yb[r[m]])).astype(np.float32).reshape(-1, H // VEC, VEC)
-        part = np.zeros(prod.shape[:2], dtype=np.float32)
-        for i in range(VEC):
-            part = (part + prod[:, :, i]).astype(np.float32)
-        grad_w[m, k] = pairwise_sum_f32(part)
+    for t in range(T):
+        for k in range(K):
+            if slot[t, k] >= 0:
+                grad_w[t, k] = dot_rn32(g[t], bf16_bits_to_f32(yb[slot[t, k]]))
     return grad_y, grad_w

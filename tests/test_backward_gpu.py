@@ -1,4 +1,7 @@
-"""GPU parity of the backward helpers against the oracle (bit-exact)."""
+"""GPU parity of the backward helpers against the oracle: the dispatch
+backward and the row gradients bit-exact, the weight gradients (a dot
+product over H channels, summed in the kernel's own order) within the
+bound of tests/tolerances.py."""
 
 import numpy as np
 import pytest
@@ -6,6 +9,7 @@ import torch
 
 import oracle
 from tests.gpu_run import SENT_BF16, gpu_layout, host, to_dev
+from tests.tolerances import assert_grad_w_close, grad_w_bound
 from workloads import make_workload, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -39,7 +43,7 @@ def run_backward(ep, idx, E, H, w, seed=0, with_w=True):
     assert np.array_equal(hgy[used], ogy[used])
     assert np.all(hgy[~used] == SENT_BF16)
     if with_w:
-        assert np.array_equal(host(gw).view(np.uint32), ogw.view(np.uint32))
+        assert_grad_w_close(host(gw), ogw, grad_w_bound(g, y, oslot), oslot)
 
 
 @pytest.mark.parametrize("name,T", [("tiny", None), ("decode", None), ("prefill", None), ("skew", 1024)])
@@ -88,4 +92,5 @@ def test_backward_wrappers(gpu):
     oslot = oracle.dispatch_layout(wl.topk_idx, wl.E)[2]
     assert np.array_equal(b(gx), oracle.dispatch_backward(b(grec), oslot))
     ogy, ogw = oracle.combine_backward(b(g), b(y), oslot, wl.topk_weights)
-    assert np.array_equal(b(gy), ogy) and np.array_equal(gw.cpu().numpy(), ogw)
+    assert np.array_equal(b(gy), ogy)
+    assert_grad_w_close(gw.cpu().numpy(), ogw, grad_w_bound(b(g), b(y), oslot), oslot)

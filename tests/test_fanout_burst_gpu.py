@@ -2,7 +2,9 @@
 in BF16 and the row gradients of ep_combine_backward.  Each 1024-lane
 workgroup (one per CU) loads up to 14 token vectors per lane and its
 tokens' receive rows first, then writes the K copies.  Against the oracle,
-bit-exact; receive rows no entry maps to keep their sentinel.
+bit-exact (the combine backward's weight gradients, a dot product in the
+kernel's own order, within the bound of tests/tolerances.py); receive rows
+no entry maps to keep their sentinel.
 
 Cases: a last workgroup with fewer tokens, top-k through a runtime count
 (10, 3), masked entries, the received routing weights, a small hidden size
@@ -15,6 +17,7 @@ import torch
 
 import oracle
 from tests.gpu_run import SENT_BF16, SENT_F32, host, to_dev
+from tests.tolerances import assert_grad_w_close, grad_w_bound
 from workloads import to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -77,4 +80,4 @@ def test_combine_backward_rows(gpu, T, K, H, mask):
     got = host(gy)
     assert np.array_equal(got[used], ogy[used])
     assert np.all(got[~used] == SENT_BF16)
-    assert np.array_equal(host(gw).view(np.uint32), ogw.view(np.uint32))
+    assert_grad_w_close(host(gw), ogw, grad_w_bound(g, y, s), s)

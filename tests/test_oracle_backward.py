@@ -4,9 +4,9 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (bf16_bits_to_f32, combine, combine_backward, dispatch_backward, dispatch_layout,
-                    pairwise_sum_f32)
-from tests.pins import f32_add, f32_mul, rn32, f32_frac
+from oracle import bf16_bits_to_f32, combine, combine_backward, dispatch_backward, dispatch_layout, dot_rn32
+from tests.pins import f32_mul, rn32, f32_frac
+from tests.tolerances import grad_w_bound
 from workloads import make_workload, to_bf16_bits
 
 
@@ -42,11 +42,11 @@ def test_combine_backward_matches_autograd(name, T):
     gyf = bf16_bits_to_f32(gy[used]).astype(np.float64)
     # two roundings of one product: binary32 then BF16
     assert np.all(np.abs(gyf - ry[used]) <= np.abs(ry[used]) * (2.0 ** -8 + 2.0 ** -23) + 1e-38)
-    # dot of H terms: 8 sequential adds + a tree of depth log2(H/8), each 2^-24
+    # the exact dot product rounded once: within half a binary32 ulp of the
+    # float64 sum, whose own error is below H * 2^-53 * sum|g*y|
     terms = np.abs(bf16_bits_to_f32(g).astype(np.float64)[:, None, :] *
                    bf16_bits_to_f32(wl.y_bits).astype(np.float64)[np.where(slot >= 0, slot, 0)]).sum(-1)
-    depth = 8 + int(np.ceil(np.log2(wl.H // 8))) + 1
-    assert np.all(np.abs(gw - rw) <= depth * 2.0 ** -24 * terms + 1e-30)
+    assert np.all(np.abs(gw - rw) <= 2.0 ** -24 * np.abs(rw) + 2.0 ** -38 * terms + 2.0 ** -149)
     assert gw[1, 0] == 0 and np.signbit(gw[1, 0]) == 0
 
 
@@ -66,27 +66,11 @@ def test_dispatch_backward_matches_autograd():
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + wl.K * 2.0 ** -24 * mag + 1e-38)
 
 
-def exact_pairwise(vals):
-    """Recursive halving over a power-of-two padded list with explicit IEEE
-    binary32 adds: an independent statement of the reduction tree."""
-    n = 1
-    while n < len(vals):
-        n *= 2
-    vals = list(vals) + [-0.0] * (n - len(vals))
-
-    def rec(lo, hi):
-        if hi - lo == 1:
-            return vals[lo]
-        mid = (lo + hi) // 2
-        return f32_add(rec(lo, mid), rec(mid, hi))
-
-    return rec(0, n)
-
-
 def test_combine_backward_exact_emulation():
-    """Element-by-element: grad_y = BF16(RN32(w*g)), grad_w by the stated order."""
+    """Element-by-element: grad_y = BF16(RN32(w*g)), grad_w = RN32 of the
+    exact rational sum of the products."""
     rng = np.random.default_rng(8)
-    T, K, H = 3, 2, 48  # 6 vectors of 8 channels: the tree pads to 8 leaves
+    T, K, H = 3, 2, 48
     g = bf16(rng.standard_normal((T, H)) * np.exp2(rng.integers(-20, 20, (T, 1))))
     y = bf16(rng.standard_normal((T * K, H)) * np.exp2(rng.integers(-20, 20, (T * K, 1))))
     w = (rng.standard_normal((T, K))).astype(np.float32)
@@ -97,33 +81,69 @@ def test_combine_backward_exact_emulation():
         for k in range(K):
             r = slot[t, k]
             if r < 0:
-                assert gw[t, k] == 0
+                assert gw[t, k] == 0 and not np.signbit(gw[t, k])
                 continue
             want_row = bf16(np.array([f32_mul(float(w[t, k]), float(v)) for v in gf[t]]))
             assert np.array_equal(gy[r], want_row)
-            parts = []
-            for v in range(H // 8):
-                acc = 0.0
-                for c in range(8 * v, 8 * v + 8):
-                    acc = f32_add(acc, f32_mul(float(gf[t, c]), float(yf[r, c])))
-                parts.append(acc)
-            assert float(gw[t, k]) == exact_pairwise(parts), (t, k)
+            exact = sum((f32_frac(gf[t, c]) * f32_frac(yf[r, c]) for c in range(H)), f32_frac(0.0))
+            assert float(gw[t, k]) == rn32(exact), (t, k)
 
 
-def test_pairwise_tree_order_is_pinned():
-    """A sum where the adjacent-pair tree and sequential order differ:
-    [2^24, 1, 1, 1] gives (2^24 + 1 -> 2^24, a tie to even) + (1 + 1) =
-    2^24 + 2 as a tree, but 2^24 sequentially (every +1 is a tie)."""
-    v = np.array([[2.0 ** 24, 1.0, 1.0, 1.0]], np.float32)
-    assert pairwise_sum_f32(v)[0] == 2.0 ** 24 + 2
+def test_grad_w_is_rounded_once():
+    """Sums where binary32 orders and the single rounding differ:
+    [2^24, 1, 1, 1] is exactly 2^24 + 3, halfway between 2^24 + 2 and
+    2^24 + 4, so it rounds to the even 2^24 + 4; adding in order keeps 2^24
+    (every +1 is a tie to even) and pairwise gives 2^24 + 2.  And 1 + 2^-24
+    + 2^-80: its nearest binary64 is the binary32 midpoint 1 + 2^-24, but
+    the exact sum lies above it, so the answer is 1 + 2^-23, not 1."""
+    a = np.array([2.0 ** 12, 1, 1, 1], np.float32)
+    assert float(dot_rn32(a, a)) == 2.0 ** 24 + 4
     seq = np.float32(0)
-    for x in v[0]:
-        seq = np.float32(seq + x)
+    for v in a * a:
+        seq = np.float32(seq + v)
     assert seq == 2.0 ** 24
-    assert exact_pairwise([2.0 ** 24, 1.0, 1.0, 1.0]) == 2.0 ** 24 + 2
-    # -0.0 padding is an identity, including for signed zeros
-    assert np.signbit(pairwise_sum_f32(np.array([[-0.0, -0.0, -0.0]], np.float32))[0])
-    assert not np.signbit(pairwise_sum_f32(np.array([[0.0, -0.0, -0.0]], np.float32))[0])
+    b = np.array([1.0, 2.0 ** -12, 2.0 ** -40], np.float32)
+    assert float(dot_rn32(b, b)) == 1.0 + 2.0 ** -23
+    assert float(dot_rn32(b[:2], b[:2])) == 1.0  # the exact tie goes to even
+    assert float(dot_rn32(-b, b)) == -(1.0 + 2.0 ** -23)
+    z = dot_rn32(np.array([1.0, -1.0], np.float32), np.array([1.0, 1.0], np.float32))
+    assert z == 0 and not np.signbit(z)
+    # the same values through combine_backward (one token, one pick)
+    g = bf16(np.concatenate([a, np.zeros(4, np.float32)])[None, :])
+    _, gw = combine_backward(g, g, np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32))
+    assert float(gw[0, 0]) == 2.0 ** 24 + 4
+
+
+def test_grad_w_tolerance_covers_shallow_orders_and_catches_slips():
+    """The GPU tolerance (tests/tolerances.py) against binary32 summation
+    orders of the stated depth: 8-channel sums then a tree, 4-channel sums
+    then a tree, on inputs with heavy cancellation, all inside the bound;
+    a result with its largest product dropped, or with y taken from another
+    row, falls outside it."""
+    rng = np.random.default_rng(21)
+    T, K, H = 64, 2, 7168
+    scale = np.exp2(rng.integers(-6, 7, (T, H)))
+    g = bf16(rng.standard_normal((T, H)) * scale)
+    y = bf16(rng.standard_normal((T * K, H)) * np.exp2(rng.integers(-6, 7, (T * K, H))))
+    slot = np.arange(T * K, dtype=np.int32).reshape(T, K)
+    _, gw = combine_backward(g, y, slot, np.ones((T, K), np.float32))
+    bound = grad_w_bound(g, y, slot)
+    gf, yf = bf16_bits_to_f32(g), bf16_bits_to_f32(y)
+    prod = (gf[:, None, :] * yf[slot]).astype(np.float32)  # exact
+    for vec in (8, 4):
+        part = np.zeros((T, K, H // vec), np.float32)
+        for i in range(vec):
+            part = (part + prod[:, :, i::vec]).astype(np.float32)
+        while part.shape[-1] > 1:
+            if part.shape[-1] % 2:
+                part = np.concatenate([part, np.full(part.shape[:-1] + (1,), -0.0, np.float32)], -1)
+            part = (part[..., 0::2] + part[..., 1::2]).astype(np.float32)
+        assert np.all(np.abs(part[..., 0].astype(np.float64) - gw) <= bound), vec
+    # the largest product dropped
+    top = np.take_along_axis(prod, np.abs(prod).argmax(-1)[..., None], -1)[..., 0].astype(np.float64)
+    assert np.all(np.abs((gw - top) - gw) > bound)
+    _, gw_wrong = combine_backward(g, y, slot[:, ::-1].copy(), np.ones((T, K), np.float32))
+    assert np.all(np.abs(gw_wrong.astype(np.float64) - gw) > bound)
 
 
 def test_dispatch_backward_order_sensitive():

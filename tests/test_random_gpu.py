@@ -1,6 +1,8 @@
-"""Seeded random shapes (128 seeds) through every entry point, bit-exact against the
+"""Seeded random shapes (128 seeds) through every entry point against the
 oracle: packed and padded layouts, FP8 and BF16 dispatch, combine, and
-both backward helpers."""
+both backward helpers bit-exact, except combine_backward's weight
+gradients (a dot product in the kernel's own order), which must lie
+within the bound of tests/tolerances.py."""
 
 import numpy as np
 import pytest
@@ -8,6 +10,7 @@ import torch
 
 import oracle
 from tests.gpu_run import SENT_BF16, SENT_F32, SENT_I32, SENT_U8, gpu_layout, host, to_dev
+from tests.tolerances import assert_grad_w_close, grad_w_bound
 from workloads import to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -79,7 +82,7 @@ def test_random_shapes(gpu, seed):
     ep.ep_combine_backward(to_dev(g.view(np.int16)), d_y, slot, d_w, gy, gw)
     ogy, ogw = oracle.combine_backward(g, y, os_, w)
     assert np.array_equal(host(gy)[:nv], ogy[:nv])
-    assert np.array_equal(host(gw).view(np.uint32), ogw.view(np.uint32))
+    assert_grad_w_close(host(gw), ogw, grad_w_bound(g, y, os_), os_)
 
     # padded layout and a dispatch / combine through it
     pc = torch.full((E,), SENT_I32, dtype=torch.int32, device="cuda")
