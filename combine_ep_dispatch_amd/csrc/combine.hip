@@ -34,6 +34,7 @@
 // Gathered bytes from which the streaming accesses are used.
 constexpr size_t kStreamingBytes = size_t(64) << 20;
 
+#include "burst_plan.h"
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -167,14 +168,11 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w
   // burst: large batches, one workgroup per CU, in equal token slices of at
   // most one held round each
   const int cus = nt ? device_cu_count() : 0;
-  const int tpb_max = static_cast<int>(static_cast<uint32_t>(kBurstItems * kBurstThreads) / vpt);
-  if (cus > 0 && tpb_max > 0) {
-    const int64_t per_launch = static_cast<int64_t>(cus) * tpb_max;
-    const int launches = static_cast<int>((T + per_launch - 1) / per_launch);
-    const int slice = (T + launches - 1) / launches;
-    for (int t0 = 0; t0 < T; t0 += slice) {
-      const int Ts = min(slice, T - t0);
-      const int tpb = (Ts + cus - 1) / cus;
+  const BurstPlan plan = burst_plan(T, vpt, kBurstItems, kBurstThreads, cus, 0, 0);
+  if (plan.launches > 0) {
+    for (int t0 = 0; t0 < T; t0 += plan.slice) {
+      const int Ts = min(plan.slice, T - t0);
+      const int tpb = burst_tpb(Ts, cus);
       const dim3 bgrid((Ts + tpb - 1) / tpb), bblock(kBurstThreads);
       const int32_t* sl = slot + static_cast<size_t>(t0) * K;
       const float* ws = w != nullptr ? w + static_cast<size_t>(t0) * K : nullptr;

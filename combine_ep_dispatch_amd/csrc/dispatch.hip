@@ -24,6 +24,7 @@
 // Not ALU-bound: replacing the division by a reciprocal multiply is not
 // measurably faster.  No LDS, no MFMA.
 
+#include "burst_plan.h"
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -259,19 +260,17 @@ bool launch_fanout_burst_bf16(const uint16_t* x, const int32_t* slot, const floa
                               hipError_t* err) {
   // tokens of 16 MB and more (read once, non-temporal), one workgroup per
   // CU, in equal token slices of at most kFanItems vectors per lane each
+  // (each token stages its K rows and weights in LDS: 8K bytes)
   if (static_cast<size_t>(T) * H * 2 < kStreamingTokenBytes) return false;
   const int cus = device_cu_count();
-  const int vpt = H / 8;
-  const int tpb_max = kFanItems * kFanThreads / vpt;
-  if (cus <= 0 || tpb_max <= 0) return false;
-  const int64_t per_launch = static_cast<int64_t>(cus) * tpb_max;
-  const int launches = static_cast<int>((T + per_launch - 1) / per_launch);
-  const int slice = (T + launches - 1) / launches;
-  for (int t0 = 0; t0 < T; t0 += slice) {
-    const int Ts = min(slice, T - t0);
-    const int tpb = (Ts + cus - 1) / cus;
+  const size_t lds_per_token = static_cast<size_t>(K) * 8;
+  const BurstPlan plan = burst_plan(T, H / 8, kFanItems, kFanThreads, cus, lds_per_token, kLdsLimit);
+  if (plan.launches == 0) return false;
+  for (int t0 = 0; t0 < T; t0 += plan.slice) {
+    const int Ts = min(plan.slice, T - t0);
+    const int tpb = burst_tpb(Ts, cus);
     const dim3 grid((Ts + tpb - 1) / tpb), block(kFanThreads);
-    const size_t lds = static_cast<size_t>(tpb) * K * 8;
+    const size_t lds = static_cast<size_t>(tpb) * lds_per_token;
     const int32_t* sl = slot + static_cast<size_t>(t0) * K;
     const float* ws = w != nullptr ? w + static_cast<size_t>(t0) * K : nullptr;
     const uint16_t* xs = x + static_cast<size_t>(t0) * H;

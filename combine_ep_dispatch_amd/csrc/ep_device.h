@@ -12,6 +12,9 @@ namespace ep {
 constexpr int kWave = 64;
 constexpr int kGroup = 128;  // channels per FP8 scale group
 
+// LDS one workgroup may allocate on gfx950: the CU's whole 160 KB.
+constexpr size_t kLdsLimit = 160 * 1024;
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---- wavefront primitives -------------------------------------------------

@@ -11,9 +11,6 @@ namespace ep {
 constexpr int kHistCopies = 4;  // one-launch layout: private histograms per lane & 3
 constexpr int kChunkSteps = 8;  // layout_chunk: calls of the caller's step hook
 
-// LDS one workgroup may allocate on gfx950: the CU's whole 160 KB.
-constexpr size_t kLdsLimit = 160 * 1024;
-
 // The keys of this wavefront's entries p_begin + 64*i + lane (E past
 // p_end), loaded apart from the ranking so that a caller can issue the
 // loads early.

@@ -59,28 +59,27 @@ def test_fp8_workload_parity(gpu, name, seed, over):
 
 def test_hbm_bf16_full_size(gpu):
     """T=32768, H=7168, BF16 dispatch (3.76 GB receive buffer) + combine on
-    the receive buffer itself (identity expert)."""
+    the receive buffer itself (identity expert), every output compared:
+    the receive rows against the oracle's BF16 dispatch, and all 32768 x
+    7168 combine outputs against the oracle's combine of the oracle's
+    receive rows, 1024 tokens at a time."""
     ep = gpu
     wl = make_workload("hbm", seed=0)
     print("case hbm 0", flush=True)
     slot, off, oslot = check_layout(ep, wl)
+    nv = int(off[-1])
     d_x = to_dev(wl.x_bits.view(np.int16))
     recv, _, _ = gpu_dispatch(ep, d_x, slot, None, fp8=False)
-    # property at full size: every receive row equals its source token
-    src = torch.from_numpy(oracle.dispatch_layout(wl.topk_idx, wl.E)[3].astype(np.int64)).cuda()
-    assert torch.equal(recv, d_x[src])
-    del src
+    oy = oracle.dispatch_bf16(wl.x_bits, oslot)
+    assert np.array_equal(host(recv)[:nv], oy[:nv])
     w = to_dev(wl.topk_weights)
-    out = gpu_combine(ep, recv, slot, w)
-    # sampled tokens against the oracle, one by one
-    rng = np.random.default_rng(0)
-    sample = np.sort(rng.choice(wl.T, size=384, replace=False))
-    rows = oslot[sample].ravel()
-    y_rows = host(recv[torch.from_numpy(rows.astype(np.int64)).cuda()])
-    sub_slot = np.arange(sample.size * wl.K, dtype=np.int32).reshape(sample.size, wl.K)
-    assert np.array_equal(y_rows, oracle.dispatch_bf16(wl.x_bits[sample], sub_slot))
-    oout = oracle.combine(y_rows, sub_slot, wl.topk_weights[sample])
-    assert np.array_equal(host(out)[sample], oout)
+    out = host(gpu_combine(ep, recv, slot, w))
+    del recv
+    print("case hbm 0: combine outputs", flush=True)
+    for t0 in range(0, wl.T, 1024):
+        t1 = min(wl.T, t0 + 1024)
+        want = oracle.combine(oy, oslot[t0:t1], wl.topk_weights[t0:t1])
+        assert np.array_equal(out[t0:t1], want), "tokens %d..%d" % (t0, t1)
 
 
 def test_prefill_fp8_then_bf16_combine_of_dequantised_rows(gpu):
