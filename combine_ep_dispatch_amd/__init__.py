@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     EP_ERR_UNSUPPORTED,
     EP_MAX_EXPERTS,
     EP_MAX_TOPK,
+    EP_NOALLOC_SCRATCH_BYTES,
     EP_OK,
     EP_RECV_BF16,
     EP_RECV_FP8_E4M3_G128,
@@ -34,6 +35,7 @@ from .api import (  # noqa: F401
     ep_dispatch_layout,
     ep_dispatch_layout_padded,
     ep_layout_dispatch,
+    ep_layout_dispatch_noalloc,
     ep_layout_workspace_bytes,
     layout,
     layout_padded,

@@ -19,6 +19,7 @@ EP_RECV_BF16 = 1
 
 EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 32
+EP_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 EXPORTS = (
     "ep_status_string",
@@ -30,6 +31,7 @@ EXPORTS = (
     "ep_dispatch",
     "ep_layout_dispatch",
     "ep_layout_dispatch_i64",
+    "ep_layout_dispatch_noalloc",
     "ep_combine",
     "ep_dispatch_backward",
     "ep_combine_backward",
@@ -66,6 +68,8 @@ def _load():
         getattr(lib, "ep_layout_dispatch" + suffix).argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p,
                                                                 p, p, p, sz, p]
         getattr(lib, "ep_layout_dispatch" + suffix).restype = ctypes.c_int
+    lib.ep_layout_dispatch_noalloc.argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p, p, p, p]
+    lib.ep_layout_dispatch_noalloc.restype = ctypes.c_int
     lib.ep_dispatch.argtypes = [p, i64, i32, i32, p, p, i32, p, p, p, p]
     lib.ep_dispatch.restype = ctypes.c_int
     lib.ep_combine.argtypes = [p, p, p, i64, i32, i32, p, p]

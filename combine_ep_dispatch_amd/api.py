@@ -174,13 +174,9 @@ def ep_dispatch(x, slot, topk_weights, format, recv_x, recv_scale=None, recv_wei
         recv_weight.data_ptr() if recv_weight is not None else None, _stream(stream)))
 
 
-def ep_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format, tokens_per_expert,
-                       expert_offset, slot, src_token, recv_x, recv_scale=None, recv_weight=None, workspace=None,
-                       stream=None):
-    """Layout and dispatch in one call (one launch up to 65536 entries).
-    capacity 0: packed layout (expert_offset [E+1], src_token [T*K], T*K
-    receive rows); capacity > 0: padded layout (expert_offset None,
-    src_token [E*capacity], E*capacity receive rows)."""
+def _check_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format, tokens_per_expert,
+                           expert_offset, slot, src_token, recv_x, recv_scale, recv_weight):
+    """Shape and dtype checks of ep_layout_dispatch's tensors; returns T, H, K."""
     _need(topk_idx, "topk_idx", _IDX)
     _debug_check_ids(topk_idx, num_experts)
     if topk_idx.dim() != 2:
@@ -214,6 +210,19 @@ def ep_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format,
         raise ValueError("unknown receive format %r" % (format,))
     if recv_weight is not None:
         _need(recv_weight, "recv_weight", _F32, (R,))
+    return T, H, K
+
+
+def ep_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format, tokens_per_expert,
+                       expert_offset, slot, src_token, recv_x, recv_scale=None, recv_weight=None, workspace=None,
+                       stream=None):
+    """Layout and dispatch in one call (one launch up to 65536 entries).
+    capacity 0: packed layout (expert_offset [E+1], src_token [T*K], T*K
+    receive rows); capacity > 0: padded layout (expert_offset None,
+    src_token [E*capacity], E*capacity receive rows)."""
+    T, H, K = _check_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format, tokens_per_expert,
+                                     expert_offset, slot, src_token, recv_x, recv_scale, recv_weight)
+    E, cap = int(num_experts), int(capacity)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         _need(workspace, "workspace", (torch.uint8, torch.int32))
@@ -224,6 +233,25 @@ def ep_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format,
         expert_offset.data_ptr() if expert_offset is not None else None, slot.data_ptr(), src_token.data_ptr(),
         recv_x.data_ptr(), recv_scale.data_ptr() if recv_scale is not None else None,
         recv_weight.data_ptr() if recv_weight is not None else None, ws_ptr, ws_bytes, _stream(stream)))
+
+
+def ep_layout_dispatch_noalloc(topk_idx, x, topk_weights, num_experts, capacity, format, tokens_per_expert,
+                               expert_offset, slot, src_token, recv_x, recv_scale=None, recv_weight=None,
+                               stream=None):
+    """ep_layout_dispatch without a workspace: the library's own per-GPU
+    scratch (EP_NOALLOC_SCRATCH_BYTES) holds the layout's histograms, so the
+    call allocates nothing.  int32 ids only.  Calls that overlap on one GPU
+    race on that scratch; issue them on one stream."""
+    if topk_idx.dtype != torch.int32:
+        raise TypeError("ep_layout_dispatch_noalloc takes int32 topk_idx")
+    T, H, K = _check_layout_dispatch(topk_idx, x, topk_weights, num_experts, capacity, format, tokens_per_expert,
+                                     expert_offset, slot, src_token, recv_x, recv_scale, recv_weight)
+    check("ep_layout_dispatch_noalloc", LIB.ep_layout_dispatch_noalloc(
+        topk_idx.data_ptr(), x.data_ptr(), topk_weights.data_ptr() if topk_weights is not None else None, T, H, K,
+        int(num_experts), int(capacity), int(format), tokens_per_expert.data_ptr(),
+        expert_offset.data_ptr() if expert_offset is not None else None, slot.data_ptr(), src_token.data_ptr(),
+        recv_x.data_ptr(), recv_scale.data_ptr() if recv_scale is not None else None,
+        recv_weight.data_ptr() if recv_weight is not None else None, _stream(stream)))
 
 
 def ep_combine(y, slot, topk_weights, out, stream=None, num_rows=None):

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "ep_internal.h"
 
@@ -206,16 +207,28 @@ EP_API ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, 
 namespace {
 
 template <typename Idx>
+ep_status check_layout_dispatch(const Idx* topk_idx, const void* x, const float* topk_weights, int64_t num_tokens,
+                                int32_t hidden, int32_t top_k, int32_t num_experts, int32_t capacity,
+                                int32_t format, const int32_t* tokens_per_expert, const int32_t* expert_offset,
+                                const int32_t* slot, const int32_t* src_token, const void* recv_x,
+                                const float* recv_scale, const float* recv_weight, const void* workspace,
+                                size_t workspace_bytes) {
+  ep_status st = check_layout(topk_idx, sizeof(Idx), num_tokens, top_k, num_experts, capacity, tokens_per_expert,
+                              capacity == 0 ? expert_offset : nullptr, slot, src_token, workspace,
+                              workspace_bytes);
+  if (st != EP_OK) return st;
+  return check_dispatch(x, num_tokens, hidden, top_k, topk_weights, format, recv_x, recv_scale, recv_weight);
+}
+
+template <typename Idx>
 ep_status layout_dispatch(const Idx* topk_idx, const void* x, const float* topk_weights, int64_t num_tokens,
                           int32_t hidden, int32_t top_k, int32_t num_experts, int32_t capacity, int32_t format,
                           int32_t* tokens_per_expert, int32_t* expert_offset, int32_t* slot, int32_t* src_token,
                           void* recv_x, float* recv_scale, float* recv_weight, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  ep_status st = check_layout(topk_idx, sizeof(Idx), num_tokens, top_k, num_experts, capacity, tokens_per_expert,
-                              capacity == 0 ? expert_offset : nullptr, slot, src_token, workspace,
-                              workspace_bytes);
-  if (st != EP_OK) return st;
-  st = check_dispatch(x, num_tokens, hidden, top_k, topk_weights, format, recv_x, recv_scale, recv_weight);
+  const ep_status st = check_layout_dispatch(topk_idx, x, topk_weights, num_tokens, hidden, top_k, num_experts,
+                                             capacity, format, tokens_per_expert, expert_offset, slot, src_token,
+                                             recv_x, recv_scale, recv_weight, workspace, workspace_bytes);
   if (st != EP_OK) return st;
   return from_hip(ep::launch_layout_dispatch(
       topk_idx, static_cast<const uint16_t*>(x), topk_weights, static_cast<int32_t>(num_tokens), hidden, top_k,
@@ -246,6 +259,66 @@ EP_API ep_status ep_layout_dispatch_i64(const int64_t* topk_idx, const void* x, 
   return layout_dispatch(topk_idx, x, topk_weights, num_tokens, hidden, top_k, num_experts, capacity, format,
                          tokens_per_expert, expert_offset, slot, src_token, recv_x, recv_scale, recv_weight,
                          workspace, workspace_bytes, stream);
+}
+
+// ---- the allocation-free form of ep_layout_dispatch ------------------------
+//
+// The only device scratch any kernel here uses is the per-chunk histograms of
+// the two-launch layout (beyond 65536 entries).  ep_layout_dispatch_noalloc
+// keeps them in this file-scope array instead of a caller's workspace.  Each
+// GPU the library runs on holds its own copy (at its own address) until the
+// process ends.  Host code never passes the array's name to a kernel: in host
+// code it is a stand-in, not a device address.  The device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+
+namespace {
+
+constexpr size_t kScratchBytes = EP_NOALLOC_SCRATCH_BYTES;  // (E+1) int32 per 4096-entry chunk
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of this device's scratch (nullptr if the runtime cannot
+// give it).
+void* device_scratch() {
+  static std::atomic<void*> ptrs[kMaxDevices] = {};
+  static std::mutex once;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(once);
+  p = ptrs[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// A stand-in for the scratch during the argument checks (aligned, of any
+// size, never dereferenced); the scratch's own limit is checked after them.
+void* const kCheckOnly = reinterpret_cast<void*>(uintptr_t(256));
+
+}  // namespace
+
+EP_API ep_status ep_layout_dispatch_noalloc(const int32_t* topk_idx, const void* x, const float* topk_weights,
+                                            int64_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
+                                            int32_t capacity, int32_t format, int32_t* tokens_per_expert,
+                                            int32_t* expert_offset, int32_t* slot, int32_t* src_token,
+                                            void* recv_x, float* recv_scale, float* recv_weight, void* stream) {
+  ep_status st = check_layout_dispatch(topk_idx, x, topk_weights, num_tokens, hidden, top_k, num_experts, capacity,
+                                       format, tokens_per_expert, expert_offset, slot, src_token, recv_x,
+                                       recv_scale, recv_weight, kCheckOnly, SIZE_MAX);
+  if (st != EP_OK) return st;
+  const size_t need = ep::layout_workspace_bytes(num_tokens * top_k, num_experts);
+  if (need > kScratchBytes) return EP_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = device_scratch();
+    if (ws == nullptr) return EP_ERR_HIP;
+  }
+  return layout_dispatch(topk_idx, x, topk_weights, num_tokens, hidden, top_k, num_experts, capacity, format,
+                         tokens_per_expert, expert_offset, slot, src_token, recv_x, recv_scale, recv_weight, ws,
+                         ws != nullptr ? kScratchBytes : 0, stream);
 }
 
 EP_API ep_status ep_combine(const void* y, const int32_t* slot, const float* topk_weights, int64_t num_tokens,

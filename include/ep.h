@@ -219,6 +219,32 @@ ep_status ep_layout_dispatch_i64(const int64_t* topk_idx, const void* x, const f
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * ep_layout_dispatch_noalloc - ep_layout_dispatch for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same results bit for bit, and no allocation of any kind.
+ *
+ * The layout's per-chunk histograms (the only scratch, used beyond 65536
+ * entries) live in a device array inside the library of
+ * EP_NOALLOC_SCRATCH_BYTES bytes, one copy per GPU, held until the process
+ * ends.  Shapes whose histograms do not fit, ep_layout_workspace_bytes(T,
+ * K, E) > EP_NOALLOC_SCRATCH_BYTES (e.g. beyond 1,044,480 entries at 1024
+ * experts, or 4,177,920 at 256), return EP_ERR_UNSUPPORTED before anything
+ * is launched.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (on different streams, or from threads without
+ * ordering) race on it and must be serialised by the caller, e.g. by
+ * issuing them on one stream.  No part of the array needs clearing between
+ * calls.  The first call on a device looks up the array's address there
+ * (EP_ERR_HIP if the runtime cannot give it).
+ */
+#define EP_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+ep_status ep_layout_dispatch_noalloc(const int32_t* topk_idx, const void* x, const float* topk_weights,
+                                     int64_t num_tokens, int32_t hidden, int32_t top_k, int32_t num_experts,
+                                     int32_t capacity, int32_t format, int32_t* tokens_per_expert,
+                                     int32_t* expert_offset, int32_t* slot, int32_t* src_token, void* recv_x,
+                                     float* recv_scale, float* recv_weight, void* stream);
+
+/*
  * ep_combine - reduce each token's K expert outputs back to the token.
  *
  * [P5 "典型工作流程"]: combine reduces the expert outputs back to the

@@ -222,3 +222,31 @@ def test_int64_id_calls_reject_bad_arguments(lib):
              None) == bad
     assert F(FAKE, FAKE, None, 4, 200, 2, 8, 0, fp8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
              None) == bad  # H % 128
+
+
+def test_noalloc_layout_dispatch_rejects_bad_arguments_and_oversize(lib):
+    """ep_layout_dispatch_noalloc checks what ep_layout_dispatch checks
+    (without a workspace) and refuses, before touching the device, shapes
+    whose layout histograms do not fit its fixed scratch."""
+    F = lib.LIB.ep_layout_dispatch_noalloc
+    fp8 = lib.EP_RECV_FP8_E4M3_G128
+    ok = dict(idx=FAKE, x=FAKE, w=None, T=4, H=256, K=2, E=8, cap=0, fmt=fp8, c=FAKE, o=FAKE, s=FAKE, r=FAKE,
+              rx=FAKE, rs=FAKE, rw=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return F(a["idx"], a["x"], a["w"], a["T"], a["H"], a["K"], a["E"], a["cap"], a["fmt"], a["c"], a["o"],
+                 a["s"], a["r"], a["rx"], a["rs"], a["rw"], None)
+
+    bad, uns = lib.EP_ERR_INVALID_ARG, lib.EP_ERR_UNSUPPORTED
+    assert call(K=0) == bad and call(T=-1) == bad and call(E=0) == bad
+    assert call(o=None) == bad and call(idx=None) == bad and call(rs=None) == bad
+    assert call(H=200) == bad and call(x=FAKE + 8) == bad
+    assert call(E=1025) == uns and call(K=33) == uns and call(T=1 << 20, K=8) == uns
+    # the scratch holds (E+1) int32 per 4096-entry chunk, 1 MiB in all
+    assert lib.EP_NOALLOC_SCRATCH_BYTES == 1 << 20
+    assert lib.ep_layout_workspace_bytes(1044480, 1, 1024) <= lib.EP_NOALLOC_SCRATCH_BYTES
+    assert lib.ep_layout_workspace_bytes(1044481, 1, 1024) > lib.EP_NOALLOC_SCRATCH_BYTES
+    assert call(T=1044481, K=1, E=1024, H=128) == uns
+    assert call(T=(1 << 22) // 8, K=8, E=256, H=128) == uns
+    assert call(T=1 << 19, K=8, E=8, cap=0, H=128, fmt=fp8, idx=None) == bad  # still checked first
