@@ -98,11 +98,16 @@ class Setup:
         self.idx = torch.from_numpy(wl.topk_idx).to(dev)
         self.w = torch.from_numpy(wl.topk_weights).to(dev)
         self.x = torch.from_numpy(wl.x_bits.view("int16")).to(dev)
-        g = torch.Generator(device=dev)
-        g.manual_seed(1000 + seed)
-        # expert outputs for combine: independent N(0,1) rows in BF16
+        # expert outputs for combine: the workload's own N(0,1) BF16 rows (the
+        # CPU baseline combines the same ones); the padded layout's E*capacity
+        # rows are drawn on the device instead
         if wl.fp8:
-            self.y = torch.randn((R, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            if capacity:
+                g = torch.Generator(device=dev)
+                g.manual_seed(1000 + seed)
+                self.y = torch.randn((R, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            else:
+                self.y = torch.from_numpy(wl.y_bits.view("int16")).to(dev).view(torch.bfloat16)
             self.recv = torch.empty((R, H), dtype=torch.uint8, device=dev)
             self.scale = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
             self.fmt = ep.EP_RECV_FP8_E4M3_G128
@@ -208,44 +213,44 @@ def time_steps(torch, s, steps, warmup, fused=False):
     return us_step, per, wall
 
 
-def time_distribution(torch, s, reps, flush_bytes=0):
-    """Per-step and per-call durations over `reps` steps (ep_layout_dispatch
-    then ep_combine), each step timed on its own with HIP events between
-    the calls (launch stream).
-    flush_bytes > 0: before every step a device read of that many bytes (a
-    reduction, outside the timed region) evicts the 256 MB Infinity Cache,
-    so the step starts from HBM.  A write fill would evict it too, but
-    leaves that many dirty lines whose write-back then slows the next
-    kernel (measured: the dispatch kernel 66 µs instead of 54).  Returns
-    {name: {"p10", "median", "p90"}} in µs."""
+def step_times(torch, step, reps, flush_bytes=0, warmup=3):
+    """Durations (µs) of `reps` steps, each timed on its own with one HIP
+    event before and one after it on the launch stream (no event between
+    the step's calls: an event there adds a few µs to what follows it).
+    flush_bytes > 0: before every step, outside its events, a device read of
+    that many bytes (a reduction) evicts the 256 MB Infinity Cache, so the
+    step starts from HBM.  A write fill would evict it too, but leaves that
+    many dirty lines whose write-back then slows the next kernel (measured:
+    the dispatch kernel 66 µs instead of 54)."""
     stream = torch.cuda.current_stream()
     scratch = torch.ones(flush_bytes // 4, dtype=torch.int32, device="cuda") if flush_bytes else None
-    for _ in range(3):
-        s.step_fused()
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
     marks = []
     for _ in range(reps):
         if scratch is not None:
             scratch.max()
-        m = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        m = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         m[0].record(stream)
-        s.layout_dispatch()
+        step()
         m[1].record(stream)
-        s.combine()
-        m[2].record(stream)
         marks.append(m)
     torch.cuda.synchronize()
-    series = {"step": [m[0].elapsed_time(m[2]) * 1e3 for m in marks],
-              "layout_dispatch": [m[0].elapsed_time(m[1]) * 1e3 for m in marks],
-              "combine": [m[1].elapsed_time(m[2]) * 1e3 for m in marks]}
     del scratch
+    return [m[0].elapsed_time(m[1]) * 1e3 for m in marks]
 
-    def pct(v, q):
-        v = sorted(v)
-        return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
 
-    return {k: {"p10": round(pct(v, 0.1), 2), "median": round(pct(v, 0.5), 2), "p90": round(pct(v, 0.9), 2)}
-            for k, v in series.items()}
+def pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
+
+def dist(v):
+    return {"p10": round(pct(v, 0.1), 2), "median": round(pct(v, 0.5), 2), "p90": round(pct(v, 0.9), 2)}
+
+
+FLUSH_BYTES = 512 << 20
 
 
 def time_loop(torch, fn, steps, warmup):
@@ -305,29 +310,28 @@ def read_traffic():
 
 
 def cpu_baseline(wl, budget_s):
-    """The oracle, untuned, on the same workload: whole passes (layout of all
-    T*K entries, then dispatch + combine of every token in 512-token chunks)
-    repeated until the time budget is spent.  numpy runs these ops on one
-    thread."""
-    import numpy as np
+    """The oracle, untuned, on the same arrays the GPU step uses: the layout
+    of all T*K entries, then, 512 tokens at a time, FP8 dispatch of those
+    tokens into their real receive rows (the layout's slots) and combine of
+    those tokens from the workload's expert outputs y gathered through the
+    same slots.  Whole passes repeat until the time budget is spent; numpy
+    runs these ops on one thread."""
+    import numpy as np  # noqa: F401
 
     import oracle
-    from workloads import to_bf16_bits
 
     T, H, E, K = wl.T, wl.H, wl.E, wl.K
     step_b = sum(alg_bytes(T, H, E, K, True))
     chunk = 512
-    y_chunk = to_bf16_bits(np.random.default_rng(7).standard_normal((chunk * K, H), dtype=np.float32))
-    sub_slot = np.arange(chunk * K, dtype=np.int32).reshape(chunk, K)
-    x = wl.x_bits
+    x, y, w = wl.x_bits, wl.y_bits, wl.topk_weights
+    R = T * K
     passes = 0
     t0 = time.perf_counter()
     while passes == 0 or time.perf_counter() - t0 < budget_s:
-        oracle.dispatch_layout(wl.topk_idx, E)
+        _, _, slot, _ = oracle.dispatch_layout(wl.topk_idx, E)
         for t in range(0, T, chunk):
-            n = min(chunk, T - t)
-            oracle.dispatch_fp8(x[t:t + n], sub_slot[:n])
-            oracle.combine(y_chunk, sub_slot[:n], wl.topk_weights[t:t + n])
+            oracle.dispatch_fp8(x[t:t + chunk], slot[t:t + chunk], num_rows=R)
+            oracle.combine(y, slot[t:t + chunk], w[t:t + chunk])
         passes += 1
     dt = time.perf_counter() - t0
     model = ""
@@ -338,8 +342,10 @@ def cpu_baseline(wl, budget_s):
         pass
     return {"value": round(passes * step_b / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)),
-            "sample": "%d full pass(es) of the same 4096-token workload (layout, FP8 dispatch and combine of "
-                      "every token in 512-token chunks), %.1f s, numpy single-threaded; %d host CPUs visible"
+            "sample": "%d full pass(es) over the prefill workload's own arrays (4096 tokens x 7168, top-8, "
+                      "seed 0): layout of all 32768 entries, then FP8 dispatch into the real receive rows and "
+                      "combine of the same expert outputs y the GPU combines, gathered through the real slots, "
+                      "512 tokens at a time; %.1f s, numpy single-threaded; %d host CPUs visible"
                       % (passes, dt, os.cpu_count())}
 
 
@@ -375,6 +381,9 @@ rocprofv3 --kernel-trace --stats -d OUT/prof_trace -o trace --output-format csv 
 rocprofv3 --pmc FETCH_SIZE -d OUT/prof_fetch -o fetch --output-format csv -- python3 bench.py --profile-pass
 rocprofv3 --pmc WRITE_SIZE -d OUT/prof_write -o write --output-format csv -- python3 bench.py --profile-pass
 rocprofv3 --kernel-trace --stats -d OUT/prof_decode -o decode --output-format csv -- python3 bench.py --profile-pass decode
+rocprofv3 --kernel-trace --stats -d OUT/prof_hbm_trace -o trace --output-format csv -- python3 bench.py --profile-pass hbm
+rocprofv3 --pmc FETCH_SIZE -d OUT/prof_hbm_fetch -o fetch --output-format csv -- python3 bench.py --profile-pass hbm
+rocprofv3 --pmc WRITE_SIZE -d OUT/prof_hbm_write -o write --output-format csv -- python3 bench.py --profile-pass hbm
 rocprofv3 --kernel-trace --stats -d OUT/prof_bench -o bench --output-format csv -- python3 bench.py > OUT/bench_under_rocprof.json
 python3 bench.py --summarize-profile OUT
 """
@@ -431,24 +440,43 @@ def summarize_profile(dirname):
         with open(os.path.join(PROFILES, "decode_128x7168_top8_kernel_trace.txt"), "w") as f:
             f.write("\n".join(lines) + "\n")
 
-    agg = {}
-    for sub, pat in (("prof_fetch", "*counter_collection.csv"), ("prof_write", "*counter_collection.csv")):
-        for r in rows(sub, pat):
-            agg.setdefault((short(r["Kernel_Name"]), r["Counter_Name"]), []).append(float(r["Counter_Value"]))
-    avg = {k: sum(v) / len(v) for k, v in agg.items()}
-    copy_kib = COPY_BYTES / 1024.0
-    f_fetch = copy_kib / avg[("__amd_rocclr_copyBuffer", "FETCH_SIZE")]
-    f_write = copy_kib / avg[("__amd_rocclr_copyBuffer", "WRITE_SIZE")]
+    def counters(fetch_sub, write_sub):
+        """{kernel: bytes per launch} from the two counter runs, and the
+        calibration lines (each counter scaled by what it reads for the
+        profile pass's plain 1 GiB device copy)."""
+        agg = {}
+        for sub in (fetch_sub, write_sub):
+            for r in rows(sub, "*counter_collection.csv"):
+                agg.setdefault((short(r["Kernel_Name"]), r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        avg = {k: sum(v) / len(v) for k, v in agg.items()}
+        copy_kib = COPY_BYTES / 1024.0
+        cf, cw = avg[("__amd_rocclr_copyBuffer", "FETCH_SIZE")], avg[("__amd_rocclr_copyBuffer", "WRITE_SIZE")]
+        f_fetch, f_write = copy_kib / cf, copy_kib / cw
+        cal = ["calibration: plain 1 GiB device copy (__amd_rocclr_copyBuffer) reads FETCH_SIZE %.1f KiB and "
+               "WRITE_SIZE %.1f KiB" % (cf, cw), "fetch_scale: %.4f" % f_fetch, "write_scale: %.4f" % f_write]
+        per = {}
+        for kern in {k for (k, c) in avg}:
+            fk, wk = avg.get((kern, "FETCH_SIZE")), avg.get((kern, "WRITE_SIZE"))
+            if fk is not None and wk is not None:
+                per[kern] = (fk * 1024 * f_fetch, wk * 1024 * f_write)
+        return per, cal
+
+    def traffic_lines(per, known):
+        out = []
+        for prefix, a in known:
+            for kern in sorted(k for k in per if k.startswith(prefix)):
+                fb, wb = per[kern]
+                out.append("%-58s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
+                           % (kern, fb, wb, fb + wb, a, (fb + wb) / a))
+        return out
+
+    per, cal = counters("prof_fetch", "prof_write")
     T, H, E, K = 4096, 7168, 256, 8
     alg = dict(zip(("layout", "dispatch_fp8_kernel", "combine_kernel"), alg_bytes(T, H, E, K, True)))
     alg["layout_dispatch_chunked"] = alg["layout"] + alg["dispatch_fp8_kernel"]
     lines = ["HBM traffic per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (two separate --pmc runs),",
              "prefill workload (4096 x 7168, 256 experts, top-8, FP8 dispatch, BF16 combine).", "",
-             "commands:", PROFILE_COMMANDS,
-             "calibration: plain 1 GiB device copy (__amd_rocclr_copyBuffer) reads FETCH_SIZE %.1f KiB and "
-             "WRITE_SIZE %.1f KiB" % (avg[("__amd_rocclr_copyBuffer", "FETCH_SIZE")],
-                                      avg[("__amd_rocclr_copyBuffer", "WRITE_SIZE")]),
-             "fetch_scale: %.4f" % f_fetch, "write_scale: %.4f" % f_write, ""]
+             "commands:", PROFILE_COMMANDS] + cal + [""]
     d_bwd, _ = backward_bytes(T, H, K)
     known = (("layout_fused", alg["layout"]),
              ("layout_dispatch_chunked", alg["layout_dispatch_chunked"]),
@@ -460,19 +488,8 @@ def summarize_profile(dirname):
              ("grad_rows_kernel", 2 * T * H + 8 * T * K + 2 * T * K * H),
              ("fanout_burst_bf16<true", 2 * T * H + 8 * T * K + 2 * T * K * H),  # the same, as a burst
              ("grad_weights_kernel", 2 * T * H + 2 * T * K * H + 8 * T * K))
-    for prefix, a in known:
-        for kern in sorted({k for (k, c) in avg if k.startswith(prefix)}):
-            fk, wk = avg.get((kern, "FETCH_SIZE")), avg.get((kern, "WRITE_SIZE"))
-            if fk is None or wk is None:
-                continue
-            fb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
-            lines.append("%-58s fetch %12.0f B  write %12.0f B  total %12.0f B  algorithmic %12d B  ratio %.4f"
-                         % (kern, fb, wb, fb + wb, a, (fb + wb) / a))
-    totals = {}
-    for kern in {k for (k, c) in avg}:
-        fk, wk = avg.get((kern, "FETCH_SIZE")), avg.get((kern, "WRITE_SIZE"))
-        if fk is not None and wk is not None:
-            totals[kern] = fk * 1024 * f_fetch + wk * 1024 * f_write
+    lines += traffic_lines(per, known)
+    totals = {k: f + w for k, (f, w) in per.items()}
     lines += ["", "the prefill step's kernels (combine is the roofline's dominant kernel), then the separate",
               "layout and dispatch kernels of the three-call form:"]
     lines += ["hbm_bytes_per_launch[%s]: %.0f" % (step, totals[kern]) for step, kern in PROFILED_KERNELS.items()]
@@ -483,6 +500,8 @@ def summarize_profile(dirname):
         f.write("\n".join(lines) + "\n")
     written = ["prefill_4096x7168_top8_kernel_trace.txt", "decode_128x7168_top8_kernel_trace.txt",
                os.path.basename(TRAFFIC_FILE)]
+    if rows("prof_hbm_fetch", "*counter_collection.csv"):
+        written.append(summarize_hbm(dirname, rows, short, counters, traffic_lines))
     if summarize_bench_run(dirname, rows, short):
         written.append(BENCH_RUN_FILE)
     for p in written:
@@ -491,6 +510,44 @@ def summarize_profile(dirname):
 
 
 BENCH_RUN_FILE = "prefill_4096x7168_top8_bench_run.txt"
+HBM_FILE = "hbm_32768x7168_top8_bf16_counter_traffic.txt"
+
+
+def summarize_hbm(dirname, rows, short, counters, traffic_lines):
+    """The 32768-token BF16 workload: kernel durations (trace) and HBM bytes
+    per launch (counters) of its layout kernels, its burst fan-out (8
+    launches of 4096 tokens each) and its burst combine (likewise)."""
+    T, H, E, K = 32768, 7168, 256, 8
+    lay, dis, com = alg_bytes(T, H, E, K, fp8=False)
+    slice_t = 4096
+    dis_launch = alg_bytes(slice_t, H, E, K, fp8=False)[1]
+    com_launch = alg_bytes(slice_t, H, E, K, fp8=False)[2]
+    per, cal = counters("prof_hbm_fetch", "prof_hbm_write")
+    stats = {short(r["Name"]): r for r in rows("prof_hbm_trace", "*kernel_stats.csv")}
+    lines = ["32768-token BF16 workload (32768 x 7168, 256 experts, top-8, BF16 dispatch into a 3.76 GB receive",
+             "buffer, BF16 combine of that buffer): rocprofv3 kernel durations and HBM bytes per launch from",
+             "FETCH_SIZE and WRITE_SIZE (separate --pmc runs), 5 three-call steps then 5 one-call steps after a",
+             "1 GiB device copy.  The layout is two kernels (layout_count, layout_finalize: 12TK + 8E + 4 B in",
+             "all); the BF16 dispatch and the combine each run as 8 launches of 4096 tokens (algorithmic bytes",
+             "per launch: dispatch 2*4096*H + 4*4096*K + 2*4096*K*H, combine 2*4096*K*H + 8*4096*K + 2*4096*H).",
+             "", "commands:", PROFILE_COMMANDS] + cal + ["",
+             "%-58s %6s %12s %14s" % ("kernel", "calls", "avg_us", "alg_GBs/launch")]
+    per_launch = {"layout_count": None, "layout_finalize": None, "fanout_burst_bf16<false": dis_launch,
+                  "combine_burst_kernel<8, false>": com_launch}
+    for name, r in sorted(stats.items()):
+        a = next((v for k, v in per_launch.items() if name.startswith(k)), None)
+        us = float(r["AverageNs"]) / 1e3
+        lines.append("%-58s %6s %12.2f %14s" % (name[:58], r["Calls"], us,
+                                                "%.1f" % (a / us / 1e3) if a else "-"))
+    lines += ["", "HBM bytes per launch:"]
+    lines += traffic_lines(per, (("layout_count", lay), ("layout_finalize", lay),
+                                 ("fanout_burst_bf16<false", dis_launch),
+                                 ("combine_burst_kernel<8, false>", com_launch)))
+    lines += ["(the layout kernels' ratios compare each launch with the whole layout's algorithmic bytes)",
+              "source_sha256: %s" % source_hash(KERNEL_SOURCES)]
+    with open(os.path.join(PROFILES, HBM_FILE), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return HBM_FILE
 
 
 def summarize_bench_run(dirname, rows, short):
@@ -499,6 +556,8 @@ def summarize_bench_run(dirname, rows, short):
     launches in that process, beside the HIP-event durations (kernel_us)
     that the same process printed in its JSON line."""
     stats = {short(r["Name"]): r for r in rows("prof_bench", "*kernel_stats.csv")}
+    trace = rows("prof_bench", "*kernel_trace.csv")
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
     path = os.path.join(dirname, "bench_under_rocprof.json")
     if not stats or not os.path.exists(path):
         return False
@@ -508,21 +567,47 @@ def summarize_bench_run(dirname, rows, short):
             rec = json.loads(line)
     if rec is None:
         return False
-    lines = ["The default bench command under rocprofv3 --kernel-trace --stats: the profiler's mean",
-             "duration of each prefill step kernel over all its launches in the process (the timed steps,",
-             "the per-kernel and single-step timings, warm and flushed), beside kernel_us, the means over",
-             "K back-to-back launches that the same process printed (HIP events on the launch stream).",
-             "Under the tracer every launch costs several microseconds more, which inflates the back-to-back",
-             "figure of a kernel as short as the layout (and the decode-size timings of that run); the",
-             "prefill dispatch and combine are long enough not to notice.", "", "commands:", PROFILE_COMMANDS,
-             "%-58s %6s %14s %14s %8s" % ("kernel", "calls", "rocprof_avg_us", "bench_us", "ratio")]
+    def b2b_run(kern):
+        """Durations of the longest run of consecutive launches of `kern`
+        with no other kernel between them: the back-to-back loop that
+        kernel_us times (the same kernel also runs inside steps, after
+        another kernel, where its mean differs)."""
+        best, cur = [], []
+        for r in trace:
+            if short(r["Kernel_Name"]) == kern:
+                cur.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                if len(cur) > len(best):
+                    best = list(cur)
+            else:
+                cur = []
+        return best
+
+    lines = ["The default bench command under rocprofv3 --kernel-trace --stats.  For each prefill step kernel:",
+             "the profiler's mean duration over all its launches in the process (timed steps, back-to-back",
+             "loops, single-step timings, warm and flushed, graph replays), and its mean over the launches of",
+             "the back-to-back loop that bench.py's kernel_us times (the longest run of launches of that",
+             "kernel with no other kernel between them), beside kernel_us itself (HIP events at the ends of",
+             "the loop on the launch stream: the kernel plus one launch gap).  roofline.frac is combine's",
+             "algorithmic bytes per launch over kernel_us[combine]; recomputed over the profiler's",
+             "back-to-back mean it is the 'frac_from_profile' column.  Under the tracer every launch costs",
+             "several microseconds more, which inflates the back-to-back figure of a kernel as short as the",
+             "layout; the prefill dispatch and combine are long enough not to notice.", "", "commands:",
+             PROFILE_COMMANDS,
+             "%-52s %6s %11s %6s %11s %10s %7s %9s" % ("kernel", "calls", "avg_all_us", "b2b_n", "avg_b2b_us",
+                                                     "bench_us", "ratio", "frac_prof")]
+    alg = dict(zip(("layout", "dispatch", "combine"), alg_bytes(4096, 7168, 256, 8, True)))
+    alg["layout_dispatch"] = alg["layout"] + alg["dispatch"]
     for step, kern in PROFILED_KERNELS.items():
         r = stats.get(kern)
         if r is None:
             continue
         prof_us = float(r["AverageNs"]) / 1e3
+        run = b2b_run(kern)
+        b2b_us = sum(run) / len(run) / 1e3 if run else float("nan")
         bench_us = rec["kernel_us"][step]
-        lines.append("%-58s %6s %14.2f %14.2f %8.3f" % (kern, r["Calls"], prof_us, bench_us, bench_us / prof_us))
+        lines.append("%-52s %6s %11.2f %6d %11.2f %10.2f %7.3f %9.4f"
+                     % (kern[:52], r["Calls"], prof_us, len(run), b2b_us, bench_us, bench_us / b2b_us,
+                        alg[step] / b2b_us / 1e3 / PEAK_HBM_GBS))
     lines += ["", "bench line of that run: value %s %s, us_per_step %s, roofline %s"
               % (rec["value"], rec["unit"], rec["us_per_step"], json.dumps(rec["roofline"]))]
     with open(os.path.join(PROFILES, BENCH_RUN_FILE), "w") as f:
@@ -530,31 +615,59 @@ def summarize_bench_run(dirname, rows, short):
     return True
 
 
+WORKLOAD_NOTES = {
+    "prefill": "4096 tokens x hidden 7168, 256 experts (8 groups, top-4 groups), top-8, FP8 E4M3 dispatch "
+               "(1 scale / 128 ch) + BF16 combine",
+    "skew": "4096 tokens x hidden 7168, 256 experts, top-8 from Zipf(1.2) expert popularity, Dirichlet(1) "
+            "weights, FP8 E4M3 dispatch + BF16 combine",
+    "hbm": "32768 tokens x hidden 7168, 256 experts (8 groups, top-4 groups), top-8, BF16 dispatch (3.76 GB "
+           "receive buffer) + BF16 combine of that buffer (identity expert)",
+    "decode": "128 tokens x hidden 7168, 256 experts (8 groups, top-4 groups), top-8, FP8 E4M3 dispatch + "
+              "BF16 combine",
+    "tiny": "64 tokens x hidden 256, 16 experts, top-2, FP8 E4M3 dispatch + BF16 combine",
+}
+
+
+def workload_record(ep, torch, name, steps, warmup, flushed_reps):
+    """A configuration's step (ep_layout_dispatch, then ep_combine) timed as
+    the headline is: single steps after an Infinity Cache flush (median,
+    p10, p90), K back-to-back steps warm, and each call's mean over K
+    back-to-back launches.  Rates are algorithmic bytes per second; a call's
+    `frac` is its rate over the 8 TB/s peak."""
+    s = Setup(ep, torch, name, 0)
+    wl = s.wl
+    lay_b, dis_b, com_b = s.bytes
+    total = lay_b + dis_b + com_b
+    warm_us = time_loop(torch, s.step_fused, steps, warmup)
+    fl = step_times(torch, s.step_fused, flushed_reps, FLUSH_BYTES)
+    plan = s.bare()
+    calls = {"layout_dispatch": (plan.layout_dispatch, lay_b + dis_b), "combine": (plan.combine, com_b)}
+    if wl.T * wl.K > 65536:  # the one call is then the layout kernels followed by the dispatch kernels
+        calls["layout"] = (plan.layout, lay_b)
+        calls["dispatch"] = (plan.dispatch, dis_b)
+    kus = {k: time_loop(torch, fn, steps, 1) for k, (fn, _) in calls.items()}
+    med = pct(fl, 0.5)
+    rec = {"config": {"workload": WORKLOAD_NOTES[name] + ", seed 0", "tokens": wl.T, "hidden": wl.H,
+                      "experts": wl.E, "top_k": wl.K, "dispatch": "fp8" if wl.fp8 else "bf16"},
+           "alg_bytes_per_step": total,
+           "us_per_step_flushed": dist(fl),
+           "GBs_flushed_median": round(total / med / 1e3, 1),
+           "us_per_step_warm": round(warm_us, 2),
+           "GBs_warm": round(total / warm_us / 1e3, 1),
+           "kernel_us": {k: round(v, 2) for k, v in kus.items()},
+           "kernel_alg_bytes": {k: b for k, (_, b) in calls.items()},
+           "kernel_GBs": {k: round(calls[k][1] / v / 1e3, 1) for k, v in kus.items()},
+           "kernel_frac": {k: round(calls[k][1] / v / 1e3 / PEAK_HBM_GBS, 4) for k, v in kus.items()}}
+    del s, plan
+    torch.cuda.empty_cache()
+    return rec
+
+
 def other_workload(ep, torch, args):
     """One JSON line for a non-headline configuration (same timing method)."""
-    s = Setup(ep, torch, args.workload, 0)
-    lay_b, dis_b, com_b = s.bytes
-    us_step, per_kernel, _ = time_steps(torch, s, args.steps, args.warmup)
-    graph_us = time_graph(torch, s.step, 20 if s.wl.T > 8192 else 200)
-    total = lay_b + dis_b + com_b
-    wl = s.wl
-    rec = {"metric": "step µs and algorithmic GB/s (three calls)", "workload": args.workload,
-           "config": {"tokens": wl.T, "hidden": wl.H, "experts": wl.E, "top_k": wl.K,
-                      "dispatch": "fp8" if wl.fp8 else "bf16"},
-           "us_per_step": round(us_step, 2), "us_per_step_graph": round(graph_us, 2),
-           "GBs": round(total / us_step / 1e3, 1),
-           "kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
-           "kernel_GBs": {"dispatch": round(dis_b / per_kernel["dispatch"] / 1e3, 1),
-                          "combine": round(com_b / per_kernel["combine"] / 1e3, 1)},
-           "kernel_alg_bytes": {"layout": lay_b, "dispatch": dis_b, "combine": com_b}}
-    # layout and dispatch in one call (one launch up to 65536 entries), then combine
-    fused_us = time_loop(torch, s.step_fused, args.steps, args.warmup)
-    rec["us_per_step_fused"] = round(fused_us, 2)
-    rec["GBs_fused"] = round(total / fused_us / 1e3, 1)
-    if wl.T * wl.K <= 65536:
-        plan = s.bare()
-        rec["kernel_us"]["layout_dispatch"] = round(time_loop(torch, plan.layout_dispatch, args.steps, 1), 2)
-        rec["us_per_step_fused_step_plan"] = round(time_loop(torch, plan.step, args.steps, args.warmup), 2)
+    rec = workload_record(ep, torch, args.workload, args.steps, args.warmup, args.steps)
+    rec = dict({"metric": "step µs and algorithmic GB/s (ep_layout_dispatch + ep_combine)",
+                "workload": args.workload}, **rec)
     print(json.dumps(rec), flush=True)
     return 0
 
@@ -600,16 +713,25 @@ def main():
 
     s = Setup(ep, torch, "prefill", 0)
     lay_b, dis_b, com_b = s.bytes
-    us_step, per_kernel, wall = time_steps(torch, s, args.steps, args.warmup, fused=True)
-    us_three = time_loop(torch, s.step, args.steps, args.warmup)
     total_b = lay_b + dis_b + com_b
-    gbs = total_b / (us_step * 1e-6) / 1e9
+    # the headline: K single steps, each after an Infinity Cache flush (the
+    # flush outside the step's events), median; then K back-to-back steps
+    # warm, each call's back-to-back launches, and the three-call form
+    fl = step_times(torch, s.step_fused, args.steps, FLUSH_BYTES, warmup=args.warmup)
+    us_step = pct(fl, 0.5)
+    us_warm, per_kernel, wall = time_steps(torch, s, args.steps, args.warmup, fused=True)
+    us_three = time_loop(torch, s.step, args.steps, args.warmup)
+    warm_single = step_times(torch, s.step_fused, args.steps)
     graph_us = time_graph(torch, s.step_fused, 50)
-    dist = {"warm": time_distribution(torch, s, 50), "flushed": time_distribution(torch, s, 50, 512 << 20)}
     s.backward_buffers(torch)
     db_b, cb_b = backward_bytes(s.wl.T, s.wl.H, s.wl.K)
     db_us = time_loop(torch, s.dispatch_backward, 30, 3)
     cb_us = time_loop(torch, s.combine_backward, 30, 3)
+    wl_prefill = s.wl
+    del s
+    torch.cuda.empty_cache()
+    workloads = {"skew": workload_record(ep, torch, "skew", args.steps, args.warmup, args.steps),
+                 "hbm": workload_record(ep, torch, "hbm", 10, 2, 10)}
 
     # decode: three calls (layout, dispatch, combine), then the fused form
     # (layout + dispatch in one launch, then combine), each eager through
@@ -637,7 +759,7 @@ def main():
     traffic = read_traffic()
     rec = {
         "metric": METRIC,
-        "value": round(gbs, 1),
+        "value": round(total_b / us_step / 1e3, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -646,24 +768,27 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp8-e4m3/bf16 storage, f32 arithmetic",
         "data": "synthetic",
-        "config": {"workload": "prefill: 4096 tokens x hidden 7168, 256 experts (8 groups, top-4 groups), "
-                               "top-8, FP8 E4M3 dispatch (1 scale / 128 ch) + BF16 combine, seed 0",
-                   "tokens": s.wl.T, "hidden": s.wl.H, "experts": s.wl.E, "top_k": s.wl.K},
+        "config": {"workload": "prefill: " + WORKLOAD_NOTES["prefill"] + ", seed 0",
+                   "tokens": wl_prefill.T, "hidden": wl_prefill.H, "experts": wl_prefill.E, "top_k": wl_prefill.K},
+        "value_method": "algorithmic bytes of one step (830.2 MB) / median of K single steps, each timed with HIP "
+                        "events on the launch stream after a 512 MB device read that evicts the Infinity Cache",
         "us_per_step": round(us_step, 2),
         "step": "ep_layout_dispatch (layout + FP8 dispatch, one launch) + ep_combine",
+        "us_per_step_warm": round(us_warm, 2),
+        "GBs_warm": round(total_b / us_warm / 1e3, 1),
         "us_per_step_graph": round(graph_us, 2),
         "us_per_step_three_calls": round(us_three, 2),
+        "step_distribution_us": {"flushed": dist(fl), "warm": dist(warm_single),
+                                 "note": "K steps each timed alone (events at the step's two ends only); "
+                                         "flushed: a 512 MB device read before every step"},
         "kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "kernel_us_method": "mean of K back-to-back launches of each kernel, HIP events on the launch stream "
                             "(kernel plus one launch gap); layout and dispatch are the three-call form's kernels",
         "kernel_alg_bytes": {"layout_dispatch": lay_b + dis_b, "combine": com_b, "layout": lay_b,
                              "dispatch": dis_b},
-        "step_distribution_us": dict(dist, note="50 steps each timed alone (events between the two calls); "
-                                                "flushed: a 512 MB device read before every step evicts the "
-                                                "Infinity Cache"),
-        "flushed_GBs_at_median": round(total_b / dist["flushed"]["step"]["median"] / 1e3, 1),
+        "workloads": workloads,
         "decode_us_per_step": decode[0]["fused"]["stream_step_plan"],
         "decode_step": "128 tokens x 7168, 256 experts, top-8, FP8: ep_layout_dispatch + ep_combine through "
                        "StepPlan, eager, mean of 200 back-to-back steps (HIP events on the launch stream)",
@@ -673,7 +798,12 @@ def main():
                         "combine_backward_GBs": round(cb_b / cb_us / 1e3, 1)},
         "roofline": {"bound": "hbm", "kernel": "combine", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic["combine"] if traffic else None},
+                     "traffic": traffic["combine"] if traffic else None,
+                     "achieved_method": "combine's algorithmic bytes per launch (528.7 MB, 4096 tokens) / "
+                                        "kernel_us[combine]",
+                     "traffic_source": "committed rocprofv3 FETCH_SIZE + WRITE_SIZE summary (%s), used only "
+                                       "while every kernel source hashes as it did when the counters were "
+                                       "taken" % os.path.relpath(TRAFFIC_FILE, ROOT)},
     }
     if traffic is not None:
         # each kernel's mean launch duration over the bytes the HBM counters saw
@@ -686,7 +816,7 @@ def main():
         "normal_kernels_nvlink_GBs": "153-158", "normal_kernels_rdma_GBs": "43-47",
         "low_latency_us": 163, "low_latency_rdma_GBs": "39-46"}
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(s.wl, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(wl_prefill, args.cpu_budget)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -190,9 +190,11 @@ ep_status ep_dispatch(const void* x, int64_t num_tokens, int32_t hidden, int32_t
  * write, bit for bit.  Up to 3072 entries (T*K) this is one kernel launch
  * built for the decode sizes, where launch latency dominates; up to 65536
  * entries another single launch, in which each workgroup lays out and
- * dispatches its own tokens (when the shape allows: top_k <= 64, at most 8
- * work items of each token per thread; else as beyond); beyond, the same
- * launches as the separate calls.
+ * dispatches its own tokens (when its share fits: at most 8 FP8 or 14 BF16
+ * work items per lane of 1024, at most one entry per lane, and the
+ * layout's LDS within the 160 KB of a workgroup, e.g. 4096 tokens of hidden
+ * 7168 at top-8; else as beyond); beyond, the same launches as the
+ * separate calls.
  *
  * topk_idx, tokens_per_expert, slot, src_token, workspace: as for
  *   ep_dispatch_layout (capacity == 0) or ep_dispatch_layout_padded

@@ -93,6 +93,15 @@ def test_bench_run_summary_pairs_profiler_and_bench_line(tmp_path, monkeypatch):
     stats = [{"Name": "void ep::(anonymous namespace)::%s(int)" % k, "Calls": 100, "AverageNs": ns, "MinNs": ns,
               "MaxNs": ns} for k, ns in zip(bench.PROFILED_KERNELS.values(), (54000.0, 90000.0, 9000.0, 50000.0))]
     _write_csv(str(out / "prof_bench" / "b_kernel_stats.csv"), stats)
+    # a trace: two steps (layout_dispatch, combine at 95 us), then 3
+    # back-to-back layout launches at 9 us, then 4 back-to-back combines at 90 us
+    names = {k: "void ep::(anonymous namespace)::%s(int)" % v for k, v in bench.PROFILED_KERNELS.items()}
+    seq = [("layout_dispatch", 54000), ("combine", 95000)] * 2 + [("layout", 9000)] * 3 + [("combine", 90000)] * 4
+    trace, t = [], 1000
+    for k, ns in seq:
+        trace.append({"Kernel_Name": names[k], "Start_Timestamp": t, "End_Timestamp": t + ns})
+        t += ns + 500
+    _write_csv(str(out / "prof_bench" / "b_kernel_trace.csv"), trace)
     line = {"value": 1.0, "unit": "GB/s", "us_per_step": 150.0, "roofline": {"frac": 0.7},
             "kernel_us": {"layout_dispatch": 53.0, "combine": 88.2, "layout": 9.9, "dispatch": 50.5}}
     with open(out / "bench_under_rocprof.json", "w") as f:
@@ -108,5 +117,8 @@ def test_bench_run_summary_pairs_profiler_and_bench_line(tmp_path, monkeypatch):
     assert bench.summarize_bench_run(str(out), rows, lambda n: n.replace("void ep::(anonymous namespace)::", "")
                                      .split("(")[0])
     text = open(prof / bench.BENCH_RUN_FILE).read()
-    assert bench.STEP_KERNELS["combine"] in text and " 0.980" in text  # 88.2 / 90.0
-    assert " 1.100" in text  # layout 9.9 / 9.0
+    row = next(ln for ln in text.splitlines() if ln.startswith(bench.STEP_KERNELS["combine"]))
+    assert "     4 " in row and " 90.00 " in row and " 0.980 " in row  # 4 back-to-back launches; 88.2 / 90.0
+    assert " 0.7344" in row  # 528744448 B / 90.0 us / 8000 GB/s = 0.73437
+    row = next(ln for ln in text.splitlines() if ln.startswith(bench.REF_KERNELS["layout"]))
+    assert " 1.100 " in row  # layout 9.9 / 9.0
