@@ -22,6 +22,17 @@
 // hit rows still held in the caches (measured 3.1-3.3 against 3.8 us for
 // 128 tokens, top-8, hidden 7168).  No LDS, no MFMA.
 //
+// The per-item kernel issues its K gathers with no branch: a gather under
+// a per-lane `if (row >= 0)` compiled, on gfx950, to the first two gathers,
+// a wait for them, then the other six, i.e. two memory latencies per item
+// instead of one.  Where a wavefront lies inside one token (H/8 a multiple
+// of 64) the token's slots and weights are scalar loads.  At 128 tokens,
+// top-8, hidden 7168 the kernel takes 2.84 against 3.12 us (GPU time of a
+// replayed graph of back-to-back launches, one process, bit-equal).  The
+// burst kernel keeps the branch: there the branch-free form measured the
+// same or slower (84.8 against 84.5 us; the dispatch backward 84.8 against
+// 82.7 us).
+//
 // Large batches (combine_burst_kernel): HBM moves a stream of reads alone
 // faster than one with writes mixed in, so each 1024-lane workgroup (one
 // per CU) owns ceil(T / CUs) consecutive tokens, keeps its finished output
@@ -46,8 +57,8 @@ constexpr int kBurstThreads = 1024;
 constexpr int kBurstItems = 14;  // output vectors held per lane (4 VGPRs each)
 
 // Adds the terms of k = k0 .. k0+KC-1 (those < K) to acc, in ascending k.
-// UNIT: every weight 1 (wrow unused).
-template <int KC, bool UNIT, bool NT>
+// UNIT: every weight 1 (wrow unused).  UNCOND: no gather under a branch.
+template <int KC, bool UNIT, bool NT, bool UNCOND = false>
 __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y, const int32_t* __restrict__ srow,
                                                  const float* __restrict__ wrow, int k0, int K, int32_t H,
                                                  uint32_t v, float (&acc)[8]) {
@@ -60,6 +71,28 @@ __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y,
     wk[j] = UNIT ? 1.0f : (in ? wrow[k0 + j] : 0.0f);
   }
   u32x4 d[KC];
+  if constexpr (UNCOND) {
+    // every gather issued, none under a branch: a masked entry reads row 0
+    // (every y has one) and its term is replaced by +0.0; acc starts at +0.0
+    // and a sum of binary32 terms that is exactly zero is +0.0, so acc is
+    // never -0.0 and acc + 0.0 == acc: the result is that of skipping it
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(y + static_cast<size_t>(r[j] < 0 ? 0 : r[j]) * H) + v;
+      d[j] = NT ? __builtin_nontemporal_load(p) : *p;
+    }
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const bool m = r[j] < 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __fmul_rn(wk[j], bf16_lo(d[j][i])), hi = __fmul_rn(wk[j], bf16_hi(d[j][i]));
+        acc[2 * i] = __fadd_rn(acc[2 * i], m ? 0.0f : lo);
+        acc[2 * i + 1] = __fadd_rn(acc[2 * i + 1], m ? 0.0f : hi);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
     d[j] = u32x4{0, 0, 0, 0};
@@ -81,7 +114,7 @@ __device__ __forceinline__ void accumulate_chunk(const uint16_t* __restrict__ y,
 
 // UNIT: no weights (every weight 1), the backward of dispatch; a separate
 // instantiation so profiles tell the two uses apart.  NT: streaming accesses.
-template <int KT, bool UNIT, bool NT>
+template <int KT, bool UNIT, bool NT, bool WU = false>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __restrict__ y,
                                                            const int32_t* __restrict__ slot,
                                                            const float* __restrict__ w, uint32_t n_items,
@@ -90,7 +123,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
   const int K = KT > 0 ? KT : Krt;
   const uint32_t item = blockIdx.x * kThreads + threadIdx.x;
   if (item >= n_items) return;
-  const uint32_t t = item / vpt;
+  // WU: every wavefront lies inside one token (vpt a multiple of 64), so the
+  // token index is wave-uniform and its slots and weights are scalar loads
+  const uint32_t t = WU ? __builtin_amdgcn_readfirstlane(item / vpt) : item / vpt;
   const uint32_t v = item - t * vpt;  // 8-channel vector within the token
   const int32_t* srow = slot + static_cast<size_t>(t) * K;
   const float* wrow = UNIT ? nullptr : w + static_cast<size_t>(t) * K;
@@ -99,9 +134,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
   if (KT > 0) {
-    accumulate_chunk<(KT > 0 ? KT : 1), UNIT, NT>(y, srow, wrow, 0, K, H, v, acc);
+    accumulate_chunk<(KT > 0 ? KT : 1), UNIT, NT, true>(y, srow, wrow, 0, K, H, v, acc);
   } else {
-    for (int k0 = 0; k0 < K; k0 += 8) accumulate_chunk<8, UNIT, NT>(y, srow, wrow, k0, K, H, v, acc);
+    for (int k0 = 0; k0 < K; k0 += 8) accumulate_chunk<8, UNIT, NT, true>(y, srow, wrow, k0, K, H, v, acc);
   }
   u32x4 o;
 #pragma unroll
@@ -196,8 +231,13 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w
     }
     return hipSuccess;
   }
-#define EP_COMBINE_NT(KV, U, NTV) \
-  hipLaunchKernelGGL((combine_kernel<KV, U, NTV>), grid, block, 0, stream, y, slot, w, n_items, vpt, H, K, out)
+#define EP_COMBINE_NT(KV, U, NTV)                                                                             \
+  if (vpt % kWave == 0)                                                                                       \
+    hipLaunchKernelGGL((combine_kernel<KV, U, NTV, true>), grid, block, 0, stream, y, slot, w, n_items, vpt, H, \
+                       K, out);                                                                               \
+  else                                                                                                        \
+    hipLaunchKernelGGL((combine_kernel<KV, U, NTV, false>), grid, block, 0, stream, y, slot, w, n_items, vpt, H, \
+                       K, out)
 #define EP_COMBINE(KV)                                                     \
   if (w == nullptr) {                                                      \
     if (nt) EP_COMBINE_NT(KV, true, true); else EP_COMBINE_NT(KV, true, false);   \
