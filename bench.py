@@ -46,7 +46,7 @@ KERNEL_SOURCES = sorted("combine_ep_dispatch_amd/csrc/" + f for f in os.listdir(
 TRAFFIC_FILE = os.path.join(PROFILES, "prefill_4096x7168_top8_counter_traffic.txt")
 # the prefill step's kernels as they appear in the profile, and the separate
 # layout and dispatch kernels of the three-call form, timed beside them
-STEP_KERNELS = {"layout_dispatch": "layout_dispatch_chunked<16, true, int, true, true, true>",
+STEP_KERNELS = {"layout_dispatch": "layout_dispatch_split<true, int, true, true, true, 7>",
                 "combine": "combine_burst_kernel<8, false>"}
 REF_KERNELS = {"layout": "layout_fused<16, true, int>", "dispatch": "dispatch_fp8_kernel<8, true, true>"}
 PROFILED_KERNELS = dict(STEP_KERNELS, **REF_KERNELS)
@@ -473,13 +473,13 @@ def summarize_profile(dirname):
     per, cal = counters("prof_fetch", "prof_write")
     T, H, E, K = 4096, 7168, 256, 8
     alg = dict(zip(("layout", "dispatch_fp8_kernel", "combine_kernel"), alg_bytes(T, H, E, K, True)))
-    alg["layout_dispatch_chunked"] = alg["layout"] + alg["dispatch_fp8_kernel"]
+    alg["layout_dispatch_split"] = alg["layout"] + alg["dispatch_fp8_kernel"]
     lines = ["HBM traffic per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (two separate --pmc runs),",
              "prefill workload (4096 x 7168, 256 experts, top-8, FP8 dispatch, BF16 combine).", "",
              "commands:", PROFILE_COMMANDS] + cal + [""]
     d_bwd, _ = backward_bytes(T, H, K)
     known = (("layout_fused", alg["layout"]),
-             ("layout_dispatch_chunked", alg["layout_dispatch_chunked"]),
+             ("layout_dispatch_split", alg["layout_dispatch_split"]),
              ("dispatch_fp8_kernel", alg["dispatch_fp8_kernel"]),
              ("combine_kernel<8, false,", alg["combine_kernel"]),
              ("combine_burst_kernel<8, false>", alg["combine_kernel"]),
@@ -567,26 +567,27 @@ def summarize_bench_run(dirname, rows, short):
             rec = json.loads(line)
     if rec is None:
         return False
-    def b2b_run(kern):
-        """Durations of the longest run of consecutive launches of `kern`
-        with no other kernel between them: the back-to-back loop that
-        kernel_us times (the same kernel also runs inside steps, after
-        another kernel, where its mean differs)."""
-        best, cur = [], []
-        for r in trace:
-            if short(r["Kernel_Name"]) == kern:
+    def b2b_run(kern, at_least):
+        """Durations of the first run of at least `at_least` consecutive
+        launches of `kern` with no other kernel between them: the prefill
+        back-to-back loop that kernel_us times (the same kernel also runs
+        inside steps, after another kernel, where its mean differs, and
+        later in the run for other workloads)."""
+        cur = []
+        for r in trace + [None]:
+            if r is not None and short(r["Kernel_Name"]) == kern:
                 cur.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-                if len(cur) > len(best):
-                    best = list(cur)
-            else:
-                cur = []
-        return best
+                continue
+            if len(cur) >= at_least:
+                return cur
+            cur = []
+        return []
 
     lines = ["The default bench command under rocprofv3 --kernel-trace --stats.  For each prefill step kernel:",
              "the profiler's mean duration over all its launches in the process (timed steps, back-to-back",
              "loops, single-step timings, warm and flushed, graph replays), and its mean over the launches of",
-             "the back-to-back loop that bench.py's kernel_us times (the longest run of launches of that",
-             "kernel with no other kernel between them), beside kernel_us itself (HIP events at the ends of",
+             "the back-to-back loop that bench.py's kernel_us times (the first run of at least K launches of",
+             "that kernel with no other kernel between them), beside kernel_us itself (HIP events at the ends of",
              "the loop on the launch stream: the kernel plus one launch gap).  roofline.frac is combine's",
              "algorithmic bytes per launch over kernel_us[combine]; recomputed over the profiler's",
              "back-to-back mean it is the 'frac_from_profile' column.  Under the tracer every launch costs",
@@ -602,7 +603,7 @@ def summarize_bench_run(dirname, rows, short):
         if r is None:
             continue
         prof_us = float(r["AverageNs"]) / 1e3
-        run = b2b_run(kern)
+        run = b2b_run(kern, rec["steps"])
         b2b_us = sum(run) / len(run) / 1e3 if run else float("nan")
         bench_us = rec["kernel_us"][step]
         lines.append("%-52s %6s %11.2f %6d %11.2f %10.2f %7.3f %9.4f"

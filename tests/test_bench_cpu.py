@@ -96,13 +96,14 @@ def test_bench_run_summary_pairs_profiler_and_bench_line(tmp_path, monkeypatch):
     # a trace: two steps (layout_dispatch, combine at 95 us), then 3
     # back-to-back layout launches at 9 us, then 4 back-to-back combines at 90 us
     names = {k: "void ep::(anonymous namespace)::%s(int)" % v for k, v in bench.PROFILED_KERNELS.items()}
-    seq = [("layout_dispatch", 54000), ("combine", 95000)] * 2 + [("layout", 9000)] * 3 + [("combine", 90000)] * 4
+    seq = ([("layout_dispatch", 54000), ("combine", 95000)] * 2 + [("layout", 9000)] * 3 + [("combine", 90000)] * 4
+           + [("dispatch", 50000)] + [("combine", 99000)] * 6)  # a later, longer run of another workload
     trace, t = [], 1000
     for k, ns in seq:
         trace.append({"Kernel_Name": names[k], "Start_Timestamp": t, "End_Timestamp": t + ns})
         t += ns + 500
     _write_csv(str(out / "prof_bench" / "b_kernel_trace.csv"), trace)
-    line = {"value": 1.0, "unit": "GB/s", "us_per_step": 150.0, "roofline": {"frac": 0.7},
+    line = {"value": 1.0, "unit": "GB/s", "us_per_step": 150.0, "roofline": {"frac": 0.7}, "steps": 3,
             "kernel_us": {"layout_dispatch": 53.0, "combine": 88.2, "layout": 9.9, "dispatch": 50.5}}
     with open(out / "bench_under_rocprof.json", "w") as f:
         f.write("some profiler noise\n" + json.dumps(line) + "\n")
