@@ -21,6 +21,9 @@ EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 32
 EP_NOALLOC_SCRATCH_BYTES = 1 << 20
 
+# ep_step_plan: opaque caller-owned storage of 32 uint64
+STEP_PLAN_WORDS = 32
+
 EXPORTS = (
     "ep_status_string",
     "ep_layout_workspace_bytes",
@@ -33,6 +36,9 @@ EXPORTS = (
     "ep_layout_dispatch_i64",
     "ep_layout_dispatch_noalloc",
     "ep_combine",
+    "ep_step_plan_init",
+    "ep_step_plan_layout_dispatch",
+    "ep_step_plan_combine",
     "ep_dispatch_backward",
     "ep_combine_backward",
     "ep_cast_fp8_e4m3",
@@ -74,6 +80,13 @@ def _load():
     lib.ep_dispatch.restype = ctypes.c_int
     lib.ep_combine.argtypes = [p, p, p, i64, i32, i32, p, p]
     lib.ep_combine.restype = ctypes.c_int
+    lib.ep_step_plan_init.argtypes = [p, p, i32, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p, p, p, p, sz, p,
+                                      p, p]
+    lib.ep_step_plan_init.restype = ctypes.c_int
+    lib.ep_step_plan_layout_dispatch.argtypes = [p]
+    lib.ep_step_plan_layout_dispatch.restype = ctypes.c_int
+    lib.ep_step_plan_combine.argtypes = [p]
+    lib.ep_step_plan_combine.restype = ctypes.c_int
     lib.ep_dispatch_backward.argtypes = [p, p, i64, i32, i32, p, p]
     lib.ep_dispatch_backward.restype = ctypes.c_int
     lib.ep_combine_backward.argtypes = [p, p, p, p, i64, i32, i32, p, p, p]

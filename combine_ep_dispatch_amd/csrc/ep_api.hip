@@ -321,8 +321,10 @@ EP_API ep_status ep_layout_dispatch_noalloc(const int32_t* topk_idx, const void*
                          ws != nullptr ? kScratchBytes : 0, stream);
 }
 
-EP_API ep_status ep_combine(const void* y, const int32_t* slot, const float* topk_weights, int64_t num_tokens,
-                            int32_t hidden, int32_t top_k, void* out, void* stream) {
+namespace {
+
+ep_status check_combine(const void* y, const int32_t* slot, const float* topk_weights, int64_t num_tokens,
+                        int32_t hidden, int32_t top_k, const void* out) {
   ep_status st = check_common(num_tokens, top_k);
   if (st != EP_OK) return st;
   if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARG;
@@ -331,9 +333,112 @@ EP_API ep_status ep_combine(const void* y, const int32_t* slot, const float* top
   if (!y || !slot || !topk_weights || !out) return EP_ERR_INVALID_ARG;
   if (!aligned(y, 16) || !aligned(out, 16) || !aligned(slot, 4) || !aligned(topk_weights, 4))
     return EP_ERR_INVALID_ARG;
+  return EP_OK;
+}
+
+}  // namespace
+
+EP_API ep_status ep_combine(const void* y, const int32_t* slot, const float* topk_weights, int64_t num_tokens,
+                            int32_t hidden, int32_t top_k, void* out, void* stream) {
+  const ep_status st = check_combine(y, slot, topk_weights, num_tokens, hidden, top_k, out);
+  if (st != EP_OK || num_tokens == 0) return st;
   return from_hip(ep::launch_combine(static_cast<const uint16_t*>(y), slot, topk_weights,
                                      static_cast<int32_t>(num_tokens), hidden, top_k,
                                      static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+}
+
+// ---- step plans --------------------------------------------------------------
+//
+// The arguments of one ep_layout_dispatch call and one ep_combine call,
+// checked once, kept in the caller's ep_step_plan storage.  `magic` is set
+// last, and only when every check passed, so a plan whose init failed (or
+// that was never initialised) launches nothing.
+
+namespace {
+
+constexpr uint32_t kPlanMagic = 0x45505350u;  // "EPSP"
+
+struct Plan {
+  uint32_t magic;
+  int32_t id_bytes;
+  int32_t hidden, top_k, num_experts, capacity, format, has_combine;
+  int64_t num_tokens;
+  const void* topk_idx;
+  const void* x;
+  const float* topk_weights;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* slot;
+  int32_t* src;
+  void* recv_x;
+  float* recv_scale;
+  float* recv_weight;
+  void* workspace;
+  const void* y;
+  void* out;
+  void* stream;
+};
+static_assert(sizeof(Plan) <= sizeof(ep_step_plan), "plan storage");
+static_assert(alignof(Plan) <= alignof(ep_step_plan), "plan alignment");
+
+template <typename Idx>
+ep_status plan_layout_dispatch(const Plan& p) {
+  return from_hip(ep::launch_layout_dispatch(
+      static_cast<const Idx*>(p.topk_idx), static_cast<const uint16_t*>(p.x), p.topk_weights,
+      static_cast<int32_t>(p.num_tokens), p.hidden, p.top_k, p.num_experts, p.capacity,
+      p.format == EP_RECV_FP8_E4M3_G128, p.counts, p.capacity == 0 ? p.offsets : nullptr, p.slot, p.src, p.recv_x,
+      p.recv_scale, p.recv_weight, p.workspace, static_cast<hipStream_t>(p.stream)));
+}
+
+}  // namespace
+
+EP_API ep_status ep_step_plan_init(ep_step_plan* plan, const void* topk_idx, int32_t id_bytes, const void* x,
+                                   const float* topk_weights, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                                   int32_t num_experts, int32_t capacity, int32_t format,
+                                   int32_t* tokens_per_expert, int32_t* expert_offset, int32_t* slot,
+                                   int32_t* src_token, void* recv_x, float* recv_scale, float* recv_weight,
+                                   void* workspace, size_t workspace_bytes, const void* y, void* out,
+                                   void* stream) {
+  if (plan == nullptr || !aligned(plan, alignof(ep_step_plan))) return EP_ERR_INVALID_ARG;
+  Plan* p = reinterpret_cast<Plan*>(plan);
+  p->magic = 0;
+  if (id_bytes != 4 && id_bytes != 8) return EP_ERR_INVALID_ARG;
+  ep_status st =
+      id_bytes == 4
+          ? check_layout_dispatch(static_cast<const int32_t*>(topk_idx), x, topk_weights, num_tokens, hidden,
+                                  top_k, num_experts, capacity, format, tokens_per_expert, expert_offset, slot,
+                                  src_token, recv_x, recv_scale, recv_weight, workspace, workspace_bytes)
+          : check_layout_dispatch(static_cast<const int64_t*>(topk_idx), x, topk_weights, num_tokens, hidden,
+                                  top_k, num_experts, capacity, format, tokens_per_expert, expert_offset, slot,
+                                  src_token, recv_x, recv_scale, recv_weight, workspace, workspace_bytes);
+  if (st != EP_OK) return st;
+  const bool has_combine = y != nullptr || out != nullptr;
+  if (has_combine) {
+    st = check_combine(y, slot, topk_weights, num_tokens, hidden, top_k, out);
+    if (st != EP_OK) return st;
+  }
+  *p = Plan{0,           id_bytes,     hidden, top_k,     num_experts,   capacity,   format,
+            has_combine, num_tokens,   topk_idx, x,       topk_weights,  tokens_per_expert, expert_offset,
+            slot,        src_token,    recv_x, recv_scale, recv_weight,  workspace,  y,
+            out,         stream};
+  p->magic = kPlanMagic;
+  return EP_OK;
+}
+
+EP_API ep_status ep_step_plan_layout_dispatch(const ep_step_plan* plan) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  if (p == nullptr || p->magic != kPlanMagic) return EP_ERR_INVALID_ARG;
+  return p->id_bytes == 4 ? plan_layout_dispatch<int32_t>(*p) : plan_layout_dispatch<int64_t>(*p);
+}
+
+EP_API ep_status ep_step_plan_combine(const ep_step_plan* plan) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  if (p == nullptr || p->magic != kPlanMagic) return EP_ERR_INVALID_ARG;
+  if (p->num_tokens == 0) return EP_OK;  // as ep_combine: nothing to reduce
+  if (!p->has_combine) return EP_ERR_INVALID_ARG;
+  return from_hip(ep::launch_combine(static_cast<const uint16_t*>(p->y), p->slot, p->topk_weights,
+                                     static_cast<int32_t>(p->num_tokens), p->hidden, p->top_k,
+                                     static_cast<uint16_t*>(p->out), static_cast<hipStream_t>(p->stream)));
 }
 
 EP_API ep_status ep_dispatch_backward(const void* grad_recv, const int32_t* slot, int64_t num_tokens,

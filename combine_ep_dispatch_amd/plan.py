@@ -2,16 +2,18 @@
 
 A serving loop calls layout -> dispatch -> combine on the same buffers every
 step.  ``StepPlan`` checks dtypes, shapes and devices once, allocates the
-layout workspace once and caches raw pointers and the stream handle, so a
-step costs two plain C calls, layout+dispatch and combine (which still
-validate their arguments).
+layout workspace once, and has the library check the raw arguments once
+into an ``ep_step_plan`` (C storage held here), so a step costs two C calls
+of one pointer argument each: layout+dispatch and combine.
 The kernels are the same ones the ``ep_*`` functions launch.
 """
+
+import ctypes
 
 import torch
 
 from . import api
-from ._lib import EP_RECV_BF16, EP_RECV_FP8_E4M3_G128, LIB, check
+from ._lib import EP_RECV_BF16, EP_RECV_FP8_E4M3_G128, LIB, STEP_PLAN_WORDS, check
 
 
 class StepPlan:
@@ -68,23 +70,27 @@ class StepPlan:
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.stream = api._stream(stream)
 
-        # entry points for these ids, and argument tuples built once; the C
-        # side still rejects a bad one
+        # the three-call form's entry points for these ids, and argument
+        # tuples built once; the C side still checks them on every call
         self._fn_layout = api._ids_fn("ep_dispatch_layout", topk_idx)
         self._fn_layout_padded = api._ids_fn("ep_dispatch_layout_padded", topk_idx)
-        self._fn_layout_dispatch = api._ids_fn("ep_layout_dispatch", topk_idx)
         self._layout_args = self._make_layout_args()
         self._dispatch_args = (x.data_ptr(), T, H, K, self.slot.data_ptr(), None, self.fmt, self.recv_x.data_ptr(),
                                self.recv_scale.data_ptr() if self.recv_scale is not None else None, None,
                                self.stream)
-        self._combine_args = (self.y.data_ptr(), self.slot.data_ptr(), topk_weights.data_ptr(), T, H, K,
-                              self.out.data_ptr(), self.stream)
         ws = self.workspace
-        self._layout_dispatch_args = (
-            topk_idx.data_ptr(), x.data_ptr(), None, T, H, K, E, self.capacity, self.fmt, self.counts.data_ptr(),
+        # the library's own plan of the two per-step launches
+        self._plan = (ctypes.c_uint64 * STEP_PLAN_WORDS)()
+        self._plan_ptr = ctypes.c_void_p(ctypes.addressof(self._plan))
+        check("ep_step_plan_init", LIB.ep_step_plan_init(
+            self._plan_ptr, topk_idx.data_ptr(), topk_idx.element_size(), x.data_ptr(), topk_weights.data_ptr(), T,
+            H, K, E, self.capacity, self.fmt, self.counts.data_ptr(),
             None if self.capacity else self.offsets.data_ptr(), self.slot.data_ptr(), self.src.data_ptr(),
             self.recv_x.data_ptr(), self.recv_scale.data_ptr() if self.recv_scale is not None else None, None,
-            ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, self.stream)
+            ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, self.y.data_ptr(),
+            self.out.data_ptr(), self.stream))
+        self._plan_layout_dispatch = LIB.ep_step_plan_layout_dispatch
+        self._plan_combine = LIB.ep_step_plan_combine
 
     def _make_layout_args(self):
         ws = self.workspace
@@ -109,10 +115,14 @@ class StepPlan:
 
     def layout_dispatch(self):
         """layout() and dispatch() as one call (one launch up to 65536 entries)."""
-        check("ep_layout_dispatch", self._fn_layout_dispatch(*self._layout_dispatch_args))
+        status = self._plan_layout_dispatch(self._plan_ptr)
+        if status:
+            check("ep_step_plan_layout_dispatch", status)
 
     def combine(self):
-        check("ep_combine", LIB.ep_combine(*self._combine_args))
+        status = self._plan_combine(self._plan_ptr)
+        if status:
+            check("ep_step_plan_combine", status)
 
     def step(self):
         self.layout_dispatch()

@@ -21,7 +21,8 @@
  * Conventions for every call
  *   - All array arguments are DEVICE pointers to contiguous row-major
  *     memory owned by the caller.  The library allocates nothing, keeps no
- *     state between calls and is safe to call from several host threads.
+ *     state between calls (a step plan lives in the caller's storage) and
+ *     is safe to call from several host threads.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
  *     call only enqueues work on it and returns; nothing synchronises with
  *     the host.  Results are valid once the stream reaches that point.
@@ -269,6 +270,56 @@ ep_status ep_layout_dispatch_noalloc(const int32_t* topk_idx, const void* x, con
 ep_status ep_combine(const void* y, const int32_t* slot, const float* topk_weights,
                      int64_t num_tokens, int32_t hidden, int32_t top_k, void* out,
                      void* stream);
+
+/*
+ * ep_step_plan - one MoE step's two launches with their arguments checked
+ * once.
+ *
+ * [P4 "使用示例 › 推理解码阶段的应用"] runs dispatch, the expert GEMMs and
+ * combine once per decoding step, on buffers that stay the same from step
+ * to step.  A plan records the arguments of one ep_layout_dispatch call
+ * (int32 or int64 ids) and of the ep_combine call on the same tokens,
+ * checked by ep_step_plan_init, so that each step's launches take one
+ * pointer each.  At decode sizes the host cost of a call (the argument
+ * checks, and marshalling many arguments from an interpreter) is of the
+ * order of the kernels' few microseconds of GPU time.
+ *
+ * The plan is plain data in caller-owned storage: the library allocates
+ * nothing, and a plan may be copied.  It records pointers only: the
+ * buffers must outlive its use, and their contents may change from step
+ * to step.  A plan's launches behave exactly as the calls it records.
+ */
+typedef struct {
+  uint64_t opaque[32];
+} ep_step_plan;
+
+/*
+ * ep_step_plan_init - check and record a step's arguments.
+ *
+ * id_bytes: 4 for int32 topk_idx, 8 for int64 (8-byte aligned).  The
+ * arguments from topk_idx to workspace_bytes, and stream, are those of
+ * ep_layout_dispatch; y and out are those of ep_combine, whose slot,
+ * topk_weights, T, H and K are the ones given here.  topk_weights feeds
+ * combine, and the dispatch only when recv_weight is given.  y and out may
+ * both be NULL for a plan that only lays out and dispatches.
+ * Returns what ep_layout_dispatch or ep_combine would return for a bad
+ * argument (EP_ERR_INVALID_ARG also for a NULL or misaligned plan or
+ * another id_bytes); a plan whose init failed launches nothing (its calls
+ * return EP_ERR_INVALID_ARG).  Pure host function.
+ */
+ep_status ep_step_plan_init(ep_step_plan* plan, const void* topk_idx, int32_t id_bytes, const void* x,
+                            const float* topk_weights, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                            int32_t num_experts, int32_t capacity, int32_t format, int32_t* tokens_per_expert,
+                            int32_t* expert_offset, int32_t* slot, int32_t* src_token, void* recv_x,
+                            float* recv_scale, float* recv_weight, void* workspace, size_t workspace_bytes,
+                            const void* y, void* out, void* stream);
+
+/* The plan's ep_layout_dispatch launch. */
+ep_status ep_step_plan_layout_dispatch(const ep_step_plan* plan);
+
+/* The plan's ep_combine launch; EP_ERR_INVALID_ARG for a plan without y
+ * and out (unless T == 0, where there is nothing to reduce). */
+ep_status ep_step_plan_combine(const ep_step_plan* plan);
 
 /*
  * ep_dispatch_backward - gradient of dispatch w.r.t. the tokens.

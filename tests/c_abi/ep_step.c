@@ -7,7 +7,9 @@
  * Reads DIR/topk_idx.bin (int32 [T,K]), DIR/x.bin (bf16 bits [T,H]),
  * DIR/w.bin (float32 [T,K]) and DIR/y.bin (bf16 bits [rows,H]; rows = T*K,
  * or E*CAPACITY when CAPACITY > 0).  MODE 0 runs the layout call then
- * ep_dispatch; MODE 1 runs ep_layout_dispatch.  Both then run ep_combine.
+ * ep_dispatch; MODE 1 runs ep_layout_dispatch; both then run ep_combine.
+ * MODE 2 records the step in an ep_step_plan and runs the plan's two
+ * launches twice, as a serving loop would.
  * With IDS64 = 1, topk_idx.bin holds int64 ids and the *_i64 layout calls
  * are used.  The FP8 receive format is used.  Writes counts.bin, offsets.bin
  * (packed only), slot.bin, src.bin, recv.bin, scale.bin, rweight.bin and
@@ -121,7 +123,15 @@ int main(int argc, char** argv) {
 
   hipStream_t stream;
   HIP_CHECK(hipStreamCreate(&stream));
-  if (mode == 1 && ids64) {
+  if (mode == 2) {
+    ep_step_plan plan;
+    EP_CHECK(ep_step_plan_init(&plan, idx, ids64 ? 8 : 4, x, w, T, H, K, E, cap, EP_RECV_FP8_E4M3_G128, counts,
+                               offsets, slot, src, recv, scale, rweight, ws, ws_bytes, y, out, stream));
+    for (int rep = 0; rep < 2; ++rep) {
+      EP_CHECK(ep_step_plan_layout_dispatch(&plan));
+      EP_CHECK(ep_step_plan_combine(&plan));
+    }
+  } else if (mode == 1 && ids64) {
     EP_CHECK(ep_layout_dispatch_i64((const int64_t*)idx, x, w, T, H, K, E, cap, EP_RECV_FP8_E4M3_G128, counts,
                                     offsets, slot, src, recv, scale, rweight, ws, ws_bytes, stream));
   } else if (mode == 1) {
@@ -139,7 +149,7 @@ int main(int argc, char** argv) {
       EP_CHECK(ep_dispatch_layout((const int32_t*)idx, T, K, E, counts, offsets, slot, src, ws, ws_bytes, stream));
     EP_CHECK(ep_dispatch(x, T, H, K, slot, w, EP_RECV_FP8_E4M3_G128, recv, scale, rweight, stream));
   }
-  EP_CHECK(ep_combine(y, slot, w, T, H, K, out, stream));
+  if (mode != 2) EP_CHECK(ep_combine(y, slot, w, T, H, K, out, stream));
   HIP_CHECK(hipStreamSynchronize(stream));
 
   write_file(dir, "counts.bin", counts, (size_t)E * 4);

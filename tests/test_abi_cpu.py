@@ -250,3 +250,42 @@ def test_noalloc_layout_dispatch_rejects_bad_arguments_and_oversize(lib):
     assert call(T=1044481, K=1, E=1024, H=128) == uns
     assert call(T=(1 << 22) // 8, K=8, E=256, H=128) == uns
     assert call(T=1 << 19, K=8, E=8, cap=0, H=128, fmt=fp8, idx=None) == bad  # still checked first
+
+
+def test_step_plan_init_checks_and_guards(lib):
+    """ep_step_plan_init checks what ep_layout_dispatch and ep_combine check;
+    a plan that was never initialised, or whose init failed, launches
+    nothing.  (Only host paths run: no plan here reaches a launch.)"""
+    L = lib.LIB
+    plan = (ctypes.c_uint64 * lib._lib.STEP_PLAN_WORDS)()
+    pp = ctypes.c_void_p(ctypes.addressof(plan))
+    fp8 = lib.EP_RECV_FP8_E4M3_G128
+    ok = dict(idx=FAKE, ib=4, x=FAKE, w=FAKE, T=4, H=256, K=2, E=8, cap=0, fmt=fp8, c=FAKE, o=FAKE, s=FAKE, r=FAKE,
+              rx=FAKE, rs=FAKE, rw=None, ws=None, wsb=0, y=FAKE, out=FAKE)
+
+    def init(**kw):
+        a = dict(ok, **kw)
+        return L.ep_step_plan_init(pp, a["idx"], a["ib"], a["x"], a["w"], a["T"], a["H"], a["K"], a["E"], a["cap"],
+                                   a["fmt"], a["c"], a["o"], a["s"], a["r"], a["rx"], a["rs"], a["rw"], a["ws"],
+                                   a["wsb"], a["y"], a["out"], None)
+
+    bad, uns = lib.EP_ERR_INVALID_ARG, lib.EP_ERR_UNSUPPORTED
+    # never initialised: zero storage launches nothing
+    assert L.ep_step_plan_layout_dispatch(pp) == bad and L.ep_step_plan_combine(pp) == bad
+    assert L.ep_step_plan_layout_dispatch(None) == bad and L.ep_step_plan_combine(None) == bad
+    assert L.ep_step_plan_init(None, FAKE, 4, FAKE, FAKE, 4, 256, 2, 8, 0, fp8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               None, None, 0, FAKE, FAKE, None) == bad
+    assert init() == lib.EP_OK
+    assert init(ib=2) == bad and init(ib=8, idx=FAKE + 4) == bad
+    # a failed init leaves the plan unusable, even after a good one
+    assert L.ep_step_plan_layout_dispatch(pp) == bad and L.ep_step_plan_combine(pp) == bad
+    # the layout + dispatch checks
+    assert init(K=0) == bad and init(E=1025) == uns and init(o=None) == bad and init(rs=None) == bad
+    assert init(H=200) == bad and init(x=FAKE + 8) == bad and init(T=8200, K=8, E=256) == bad
+    # the combine checks: y and out both or neither; weights; alignment
+    assert init(y=None) == bad and init(out=None) == bad and init(out=FAKE + 2) == bad
+    assert init(w=None) == bad
+    assert init(y=None, out=None) == lib.EP_OK      # layout + dispatch only
+    assert L.ep_step_plan_combine(pp) == bad        # ... so no combine
+    assert init(T=0, y=None, out=None, w=None) == lib.EP_OK
+    assert L.ep_step_plan_combine(pp) == lib.EP_OK  # an empty batch: nothing to reduce

@@ -23,9 +23,12 @@ EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "ep_step
 @pytest.mark.parametrize("ids64", [False, True])
 @pytest.mark.parametrize("name,T,cap,mode", [("decode", None, 0, 0), ("decode", None, 0, 1), ("decode", None, 128, 0),
                                              ("decode", None, 128, 1), ("tiny", None, 0, 1), ("tiny", None, 3, 1),
-                                             ("prefill", 600, 0, 0), ("prefill", 600, 0, 1)])
+                                             ("prefill", 600, 0, 0), ("prefill", 600, 0, 1), ("decode", None, 0, 2),
+                                             ("decode", None, 128, 2), ("tiny", None, 3, 2), ("prefill", 600, 0, 2)])
 def test_c_driver_matches_oracle(gpu, tmp_path, name, T, cap, mode, ids64):
-    """ids64: int64 expert ids through the *_i64 entry points."""
+    """mode 0: the layout call then ep_dispatch; 1: ep_layout_dispatch; 2:
+    an ep_step_plan, its two launches run twice.  ids64: int64 expert ids
+    through the *_i64 entry points (mode 2: id_bytes 8)."""
     assert os.path.exists(EXE), "C driver not built: run `python tests/c_abi/build.py`"
     wl = make_workload(name, seed=11, T=T)
     T, H, E, K = wl.T, wl.H, wl.E, wl.K

@@ -117,6 +117,58 @@ def test_layout_path_boundaries(gpu, rows, E):
     assert np.array_equal(host(slot), os_) and np.array_equal(host(src), osrc)
 
 
+def special_groups(rng, n, first=0):
+    """n groups of 128 channels (float32, exact in BF16 where it matters),
+    group i of pattern (first + i) % 13: zeros; signed zeros; a wide
+    dynamic range; BF16 subnormals; +-3e38; 448 with an E4M3 tie; 2^-140;
+    1e-30 scale; amax exactly 2^-80 with channels down to the BF16
+    subnormals (the quantiser's shared-reciprocal path); amax just below
+    2^-80 (its plain-division path); E4M3 ties after division by s = 3;
+    normals at 2^-79; plain normals."""
+    out = np.empty((n, 128), np.float32)
+    for i in range(n):
+        g = rng.standard_normal(128).astype(np.float32)
+        sign = np.where(rng.random(128) < 0.5, -1.0, 1.0).astype(np.float32)
+        spread = (2.0 ** -rng.uniform(0.0, 53.0, 128)).astype(np.float32)
+        p = (first + i) % 13
+        if p == 0:
+            g[:] = 0.0
+        elif p == 1:
+            g[:] = sign * np.float32(0.0)
+        elif p == 2:
+            g *= np.float32(1e-3)
+            g[5] = 300.0
+        elif p == 3:
+            g *= np.float32(2.0 ** -130)
+        elif p == 4:
+            g = sign * np.float32(3.0e38)
+        elif p == 5:
+            g[:] = 448.0
+            g[1::7] = 1.0625
+        elif p == 6:
+            g[:] = np.float32(2.0 ** -140)
+        elif p == 7:
+            g *= np.float32(1e-30)
+        elif p == 8:
+            g = sign * np.float32(2.0 ** -80) * spread
+            g[3] = np.float32(2.0 ** -80)
+        elif p == 9:
+            g = sign * np.float32(float.fromhex("0x1.fep-81")) * spread
+            g[3] = -np.float32(float.fromhex("0x1.fep-81"))
+        elif p == 10:
+            ties = np.array([1.0625, 1.1875, 1.3125, 1.5625, 1.9375, 4.5 / 512, 0.5625, 0.03125 * 1.0625], np.float32)
+            g = sign * np.float32(3.0) * ties[np.arange(128) % ties.size]
+            g[0] = 1344.0
+        elif p == 11:
+            g *= np.float32(2.0 ** -79)
+        out[i] = g
+    return out
+
+
+def special_tokens(rng, T, H):
+    return special_groups(rng, T * H // 128).reshape(T, H)
+
+
 def test_special_values(gpu):
     """Zero groups, signed zeros, FP8-subnormal outputs, BF16 subnormal
     inputs, the 2^-126 scale floor, huge magnitudes, exact ties."""
@@ -135,6 +187,7 @@ def test_special_values(gpu):
     x[5, 1] = np.float32(1.0625 * 448 / 448)  # E4M3 tie after division by s = 1
     x[6, :128] = np.float32(2.0 ** -140)
     x[7, :] = np.float32(1e-30) * x[7, :]
+    x[8:12, :128] = special_groups(rng, 4, first=8)  # around amax = 2^-80, and E4M3 ties with s = 3
     xb = to_bf16_bits(x)
     idx = np.stack([np.arange(T) % 5, (np.arange(T) + 2) % 5], axis=1).astype(np.int32)
     w = rng.standard_normal((T, 2)).astype(np.float32)
@@ -234,3 +287,18 @@ def test_scale_store_paths(gpu, T, H, scale_offset, K):
     # nothing written outside the scale rows of valid entries
     rest = host(store)
     assert np.all(rest[:scale_offset] == -3.0) and np.all(rest[scale_offset + nv * G:] == -3.0)
+
+
+@pytest.mark.parametrize("T,H", [(16, 512), (128, 7168), (1000, 7168), (4096, 7168)])
+def test_special_values_one_call(gpu, T, H):
+    """The special-value groups through ep_layout_dispatch on each of its
+    kernels: the decode kernel (16 and 128 tokens), the chunked kernel
+    (1000 tokens) and the split kernel (4096 tokens of hidden 7168)."""
+    from tests.test_chunked_gpu import routing, run_and_check
+    rng = np.random.default_rng(T + H)
+    idx = routing(rng, T, 8, 256, mask_frac=0.02)
+    xb = to_bf16_bits(special_tokens(rng, T, H))
+    w = rng.standard_normal((T, 8)).astype(np.float32)
+    print("case special values one call T=%d H=%d" % (T, H), flush=True)
+    run_and_check(gpu, idx, xb, w, 256, 0, True)
+    run_and_check(gpu, idx, xb, w, 256, 40 if T >= 1000 else 4, True)
