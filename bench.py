@@ -290,6 +290,22 @@ def time_graph(torch, step, replays, steps_per_graph=1):
     return a.elapsed_time(b) * 1e3 / (replays * steps_per_graph)
 
 
+def host_submit_us(torch, step, n):
+    """Host time per call of `step` over n calls issued back to back (no
+    synchronisation inside the loop): when it reaches the GPU time per
+    step, eager timing measures the launches' host cost, not the kernels."""
+    import time
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        step()
+    t1 = time.perf_counter()
+    torch.cuda.synchronize()
+    return (t1 - t0) / n * 1e6
+
+
 def read_traffic():
     """HBM bytes per launch of the profiled prefill kernels (the keys of
     PROFILED_KERNELS) from the committed rocprofv3 counter summary, or None
@@ -751,6 +767,9 @@ def main():
                           # one graph launch costs more host time than this step's GPU time;
                           # ten steps in one graph amortise it
                           "graph_10_steps": round(time_graph(torch, d.step_fused, args.decode_replays // 10, 10), 2),
+                          "graph_40_steps": round(time_graph(torch, d.step_fused, max(1, args.decode_replays // 40),
+                                                             40), 2),
+                          "host_us_per_step_step_plan": round(host_submit_us(torch, plan.step, 2000), 2),
                           "kernel_us": {"layout_dispatch": round(time_loop(torch, plan.layout_dispatch, 200, 10), 2)}}
         decode[cap] = rec_d
         del d, plan
@@ -792,7 +811,10 @@ def main():
         "workloads": workloads,
         "decode_us_per_step": decode[0]["fused"]["stream_step_plan"],
         "decode_step": "128 tokens x 7168, 256 experts, top-8, FP8: ep_layout_dispatch + ep_combine through "
-                       "StepPlan, eager, mean of 200 back-to-back steps (HIP events on the launch stream)",
+                       "StepPlan, eager, mean of 200 back-to-back steps (HIP events on the launch stream); eager "
+                       "decode is host-bound (decode_128tok_us.fused.host_us_per_step_step_plan: host time to "
+                       "submit a step, about two HIP kernel launches); graph_40_steps is the GPU time per step "
+                       "with the host out of the way",
         "decode_128tok_us": dict(decode[0], low_latency_padded_128=decode[128]),
         "backward_us": {"dispatch_backward": round(db_us, 2), "combine_backward": round(cb_us, 2),
                         "dispatch_backward_GBs": round(db_b / db_us / 1e3, 1),
