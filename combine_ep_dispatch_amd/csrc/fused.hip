@@ -68,21 +68,20 @@ static_assert(static_cast<int64_t>(1025) * kFusedMaxEntries < (int64_t(1) << 31)
 constexpr int kTokenLdsInts = kMaxWaves * kMaxK + 2 * kMaxK;
 constexpr int kLdsInts = 1025 > kTokenLdsInts ? 1025 : kTokenLdsInts;
 
-// This lane's keys: entries u*blockDim + tid for u < NS, with the address
-// clamped to the last entry (n >= 1) so that all NS loads are issued back
-// to back, free of branches; lanes past n get a copy of the last key, which
-// callers mask by position.
+// This lane's keys: entries u*bs + tid for u < NS (bs: the workgroup's
+// lanes), with the address clamped to the last entry (n >= 1) so that all
+// NS loads are issued back to back, free of branches; lanes past n get a
+// copy of the last key, which callers mask by position.
 template <int NS, typename Idx>
-__device__ __forceinline__ void load_ids(const Idx* __restrict__ idx, int n, Idx (&raw)[NS]) {
-  const int bs = blockDim.x;
+__device__ __forceinline__ void load_ids(const Idx* __restrict__ idx, int n, int bs, Idx (&raw)[NS]) {
 #pragma unroll
   for (int u = 0; u < NS; ++u) raw[u] = idx[min(u * bs + static_cast<int>(threadIdx.x), n - 1)];
 }
 
 template <int NS, typename Idx>
-__device__ __forceinline__ void load_keys(const Idx* __restrict__ idx, int n, int E, int (&e)[NS]) {
+__device__ __forceinline__ void load_keys(const Idx* __restrict__ idx, int n, int E, int bs, int (&e)[NS]) {
   Idx raw[NS];
-  load_ids<NS>(idx, n, raw);
+  load_ids<NS>(idx, n, bs, raw);
 #pragma unroll
   for (int u = 0; u < NS; ++u) e[u] = expert_key(raw[u], E);
 }
@@ -90,12 +89,12 @@ __device__ __forceinline__ void load_keys(const Idx* __restrict__ idx, int n, in
 // Workgroup 0: per-expert counts (clamped to the capacity in the padded
 // layout) and, for the packed layout, the exclusive-scan offsets.
 template <int NS, typename Idx>
-__device__ void write_counts_block(const Idx* __restrict__ idx, int n, int E, int cap, int* lds,
+__device__ void write_counts_block(const Idx* __restrict__ idx, int n, int E, int cap, int bs, int* lds,
                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  const int tid = threadIdx.x, bs = blockDim.x, nk = E + 1;
+  const int tid = threadIdx.x, nk = E + 1;
   int* hist = lds;
   int e[NS];  // keys
-  if (n > 0) load_keys<NS>(idx, n, E, e);  // block-uniform; nothing to read for an empty batch
+  if (n > 0) load_keys<NS>(idx, n, E, bs, e);  // block-uniform; nothing to read for an empty batch
   for (int i = tid; i < nk; i += bs) hist[i] = 0;
   __syncthreads();
   if (n > 0) {
@@ -119,7 +118,7 @@ __device__ void write_counts_block(const Idx* __restrict__ idx, int n, int E, in
 // (uint)(code - lo) < (uint)(code_j - lo) holds exactly when
 // lo <= code < code_j, because code - lo < 0 wraps to a large value.  `code`
 // holds this lane's entry codes (INT_MAX past n); the wave's entries are
-// lane + 64*w + blockDim*u.  Lane 0 of each wave leaves its counts in LDS,
+// lane + 64*w + bs*u.  Lane 0 of each wave leaves its counts in LDS,
 // and wave 0 the targets' keys.
 template <int KC, int NS>
 __device__ __forceinline__ void count_targets(const int (&te)[KC], int p0, int k0, int K, int n, int E, bool padded,
@@ -151,28 +150,33 @@ __device__ __forceinline__ void count_targets(const int (&te)[KC], int p0, int k
   }
 }
 
-// NS: steps of blockDim entries per lane (n <= NS * blockDim).  MAXT: the
-// largest workgroup the instantiation is launched with (256, or 1024 for
+// NS: steps of bs entries per lane (n <= NS * bs).  MAXT: the largest
+// workgroup the instantiation is launched with (256, or 1024 for
 // token-wide workgroups); the tighter bound measured 0.25-0.45 us faster.
-// Idx: int32_t or int64_t expert ids.
+// Idx: int32_t or int64_t expert ids.  The workgroup size comes as an
+// argument (a constant where MAXT fixes it), not from blockDim: reading
+// blockDim makes the launch carry the runtime's implicit arguments, 256
+// bytes more that the host writes for every launch (measured host cost of
+// a launch: 2.6 us with 8 bytes of arguments, 3.5 us with 128).
 template <int KT, bool FP8, int NS, int MAXT, typename Idx>
 __global__ __launch_bounds__(MAXT) void layout_dispatch_kernel(
     const Idx* __restrict__ idx, const uint16_t* __restrict__ x, const float* __restrict__ w, int32_t T,
-    int32_t H, int32_t Krt, int32_t E, int32_t cap, uint32_t nchunk, int32_t* __restrict__ counts,
+    int32_t H, int32_t Krt, int32_t E, int32_t cap, uint32_t nchunk, int32_t bs_arg, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src, void* __restrict__ recv,
     float* __restrict__ recv_scale, float* __restrict__ recv_weight) {
   __shared__ int lds[kLdsInts];
   constexpr int KC = KT > 0 ? KT : 8;  // targets counted per pass over the ids
   const int K = KT > 0 ? KT : Krt;
   const int n = T * K;
+  const int bs = MAXT == kMinThreads ? kMinThreads : bs_arg;
   if (blockIdx.x == 0) {
-    write_counts_block<NS>(idx, n, E, cap, lds, counts, offsets);
+    write_counts_block<NS>(idx, n, E, cap, bs, lds, counts, offsets);
     return;
   }
   const uint32_t b = blockIdx.x - 1;
   const int t = static_cast<int>(b / nchunk);
   const uint32_t chunk = b - static_cast<uint32_t>(t) * nchunk;
-  const int tid = threadIdx.x, bs = blockDim.x, nw = bs / kWave;
+  const int tid = threadIdx.x, nw = bs / kWave;
   const uint32_t vpt = static_cast<uint32_t>(H) / (FP8 ? 16 : 8);
   const uint32_t v = chunk * bs + tid;  // vector within the token
   const bool active = v < vpt;
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(MAXT) void layout_dispatch_kernel(
     }
   }
   Idx raw[NS];
-  load_ids<NS>(idx, n, raw);
+  load_ids<NS>(idx, n, bs, raw);
   // keep every load above this point: the compiler would otherwise sink
   // some of them next to their first use, one memory latency after another
   asm volatile("" ::: "memory");
@@ -294,7 +298,7 @@ void launch_fused(const Idx* idx, const uint16_t* x, const float* w, int32_t T, 
   const dim3 grid(1 + static_cast<uint32_t>(T) * nchunk), block(bs);
 #define EP_FUSED(KV)                                                                                            \
   hipLaunchKernelGGL((layout_dispatch_kernel<KV, FP8, NS, MAXT, Idx>), grid, block, 0, stream, idx, x, w, T, H, K, E, cap, \
-                     nchunk, counts, offsets, slot, src, recv, recv_scale, recv_weight)
+                     nchunk, bs, counts, offsets, slot, src, recv, recv_scale, recv_weight)
   switch (K) {
     case 1: EP_FUSED(1); break;
     case 2: EP_FUSED(2); break;

@@ -47,10 +47,10 @@ constexpr int kMultiWaves = kMultiThreads / kWave;
 
 template <int ITERS, typename Idx>
 __global__ __launch_bounds__(kSingleMaxThreads) void layout_single(
-    const Idx* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t* __restrict__ counts,
+    const Idx* __restrict__ idx, int32_t R, int32_t K, int32_t E, int32_t cap, int32_t bs, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ src) {
   extern __shared__ uint64_t lds64[];
-  const int tid = threadIdx.x, bs = blockDim.x, nw = bs / kWave, w = tid / kWave;
+  const int tid = threadIdx.x, nw = bs / kWave, w = tid / kWave;  // bs: the workgroup's lanes
   const int nk = E + 1;
   uint64_t* lmask = lds64;                                // [nw][nk]
   int* cnt = reinterpret_cast<int*>(lmask + nw * nk);     // [nw][nk]
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kSingleMaxThreads) void layout_single(
   }
   __syncthreads();
   block_exclusive_scan(off, nk);
-  write_counts(off, E, cap, 0, counts, offsets);
+  write_counts(off, E, cap, 0, bs, counts, offsets);
 
   const int lane = tid & (kWave - 1);
 #pragma unroll
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kMultiThreads) void layout_finalize(
   }
   __syncthreads();
   block_exclusive_scan(off, nk);
-  write_counts(off, E, cap, b, counts, offsets);
+  write_counts(off, E, cap, b, kMultiThreads, counts, offsets);
 
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
@@ -238,7 +238,7 @@ hipError_t launch_layout(const Idx* topk_idx, int32_t rows, int32_t top_k, int32
     const dim3 grid(1), block(nw * kWave);
 #define EP_LAYOUT_SINGLE(IT)                                                                                  \
   hipLaunchKernelGGL((layout_single<IT, Idx>), grid, block, lds, stream, topk_idx, rows, top_k, E, capacity, \
-                     counts, offsets, slot, src)
+                     nw * kWave, counts, offsets, slot, src)
     if (steps <= 1) EP_LAYOUT_SINGLE(1);
     else if (steps <= 4) EP_LAYOUT_SINGLE(4);
     else EP_LAYOUT_SINGLE(16);

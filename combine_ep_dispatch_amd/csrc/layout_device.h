@@ -114,12 +114,14 @@ __device__ __forceinline__ int write_entry(int p, int k, int within, const int* 
 }
 
 // Counts and offsets from the exclusive scan `off` of the per-key totals
-// (written by one workgroup); in the padded layout the count is clamped to
-// the capacity and there are no offsets.
-__device__ __forceinline__ void write_counts(const int* off, int E, int cap, int part, int32_t* __restrict__ counts,
-                                             int32_t* __restrict__ offsets) {
+// (written by one workgroup of bs lanes); in the padded layout the count is
+// clamped to the capacity and there are no offsets.  The callers pass bs
+// rather than read blockDim, which would make every launch carry the
+// runtime's 256 bytes of implicit arguments.
+__device__ __forceinline__ void write_counts(const int* off, int E, int cap, int part, int bs,
+                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
   if (part != 0) return;
-  const int tid = threadIdx.x, bs = blockDim.x;
+  const int tid = threadIdx.x;
   for (int j = tid; j < E; j += bs) {
     const int total = off[j + 1] - off[j];
     counts[j] = cap == 0 ? total : min(total, cap);
@@ -297,7 +299,7 @@ __device__ __forceinline__ int layout_chunk(const Idx* __restrict__ idx, int32_t
   }
   __syncthreads();
   block_exclusive_scan(after, nk);
-  write_counts(after, E, cap, blockIdx.x, counts, offsets);
+  write_counts(after, E, cap, blockIdx.x, NW * kWave, counts, offsets);
 
   const int k = key[0];
   return k >= 0 ? write_entry(p_begin + lane, k, before[k] + cnt[w * nk + k] + rank[0], after, E, K, cap, slot, src)
