@@ -739,6 +739,10 @@ def main():
     us_warm, per_kernel, wall = time_steps(torch, s, args.steps, args.warmup, fused=True)
     us_three = time_loop(torch, s.step, args.steps, args.warmup)
     warm_single = step_times(torch, s.step_fused, args.steps)
+    # each call of the step timed alone, in both modes
+    call_dist = {name: {"flushed": dist(step_times(torch, fn, args.steps, FLUSH_BYTES)),
+                        "warm": dist(step_times(torch, fn, args.steps))}
+                 for name, fn in (("layout_dispatch", s.layout_dispatch), ("combine", s.combine))}
     graph_us = time_graph(torch, s.step_fused, 50)
     s.backward_buffers(torch)
     db_b, cb_b = backward_bytes(s.wl.T, s.wl.H, s.wl.K)
@@ -803,6 +807,8 @@ def main():
         "step_distribution_us": {"flushed": dist(fl), "warm": dist(warm_single),
                                  "note": "K steps each timed alone (events at the step's two ends only); "
                                          "flushed: a 512 MB device read before every step"},
+        "call_distribution_us": dict(call_dist, note="each call alone between two events, K times: p10 / "
+                                                      "median / p90; flushed as for the step"),
         "kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "kernel_us_method": "mean of K back-to-back launches of each kernel, HIP events on the launch stream "
                             "(kernel plus one launch gap); layout and dispatch are the three-call form's kernels",
