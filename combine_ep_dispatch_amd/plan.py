@@ -125,5 +125,11 @@ class StepPlan:
             check("ep_step_plan_combine", status)
 
     def step(self):
-        self.layout_dispatch()
-        self.combine()
+        """layout_dispatch() then combine(), with no Python call between the
+        two launches (at decode sizes the host's submit time paces a step)."""
+        status = self._plan_layout_dispatch(self._plan_ptr)
+        if status:
+            check("ep_step_plan_layout_dispatch", status)
+        status = self._plan_combine(self._plan_ptr)
+        if status:
+            check("ep_step_plan_combine", status)
